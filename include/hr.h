@@ -1,0 +1,242 @@
+/*
+ * hr.h -- C ABI of libhr, the MI355X (gfx950) FP16 all-reduce combine.
+ *
+ * The operation.  An all-reduce over a tensor-parallel group leaves on every
+ * rank the elementwise sum of the ranks' FP16 contributions.  libhr computes
+ * that sum as a left fold in rank order with one binary16 rounding (to
+ * nearest, ties to even) after every add:
+ *
+ *     R[i] = fl16( ... fl16( fl16(x0[i] + x1[i]) + x2[i] ) ... + x_{G-1}[i] )
+ *
+ * For two ranks this is the single-rounding, commutative FP16 sum that the
+ * 1Cat-vLLM pull request "[Kernel] Two-rank FP16 all-reduce through pinned
+ * host memory for GPUs without P2P" describes (section "Purpose"); both ranks
+ * obtain identical bits.  For more ranks the pages fix no order; the SGLang
+ * pull request "[SM120] Add optional FlashInfer PCIe-IPC all-reduce for
+ * switch-free hosts" (section "Accuracy") shows that the order changes bits,
+ * so libhr fixes the left fold in increasing rank index.  NaN payloads are
+ * whatever the hardware add produces; every other result is exact to the
+ * definition above.
+ *
+ * Two entry points compute it:
+ *
+ *  - hr_reduce_f16: G contributions already resident in device memory (HBM)
+ *    are folded into one output buffer by one kernel launch.
+ *
+ *  - hr_allreduce_f16: a two-rank exchange through a channel.  Each rank's
+ *    kernel writes its contribution into pinned, device-mapped host memory,
+ *    raises a per-workgroup ready flag, waits for the peer's flag and adds
+ *    the peer's values, exactly as the 1Cat-vLLM page's "Purpose" section
+ *    lays out: one kernel per call, no CPU work, no stream synchronisation,
+ *    so the call can be captured into a hipGraph; host slots are double
+ *    buffered by call parity.  The channel is a handle so that one process
+ *    can own several two-rank groups (same section).  Both ranks of a
+ *    channel may live in one process on one GPU ("loopback": two
+ *    concurrently running launches on two streams).
+ *
+ * Conventions for every function:
+ *  - Every function returns an hr_status; nothing throws across the ABI.
+ *  - Device pointers are plain HIP device addresses (hipMalloc memory or any
+ *    allocator built on it); buffers hold IEEE binary16 values, contiguous,
+ *    element i at byte offset 2*i.  The caller owns them and keeps them alive
+ *    until the work queued on the stream has finished.
+ *  - A stream argument is a hipStream_t; NULL selects the null stream of the
+ *    current device.  Calls only enqueue work on that stream: they never
+ *    synchronise, allocate or copy, so they may be captured into a graph.
+ *  - Argument errors are reported synchronously, before anything is
+ *    enqueued, and leave all state unchanged.
+ */
+#ifndef HR_H
+#define HR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(HR_BUILDING_LIBRARY)
+#define HR_API __attribute__((visibility("default")))
+#else
+#define HR_API
+#endif
+
+/* Same tag as hipStream_t, so a hipStream_t converts without a cast. */
+typedef struct ihipStream_t *hr_stream_t;
+
+/* Opaque channel handle; the library owns everything behind it. */
+typedef struct hr_channel_s *hr_channel;
+
+typedef enum {
+    HR_OK = 0,
+    HR_ERR_INVALID_ARG = 1,  /* null pointer, bad rank/G, partial overlap  */
+    HR_ERR_ALIGNMENT = 2,    /* a binary16 pointer that is not 2-byte aligned */
+    HR_ERR_TOO_LARGE = 3,    /* numel above the channel's max_numel          */
+    HR_ERR_UNSUPPORTED = 4,  /* world_size other than 2, device unusable     */
+    HR_ERR_HIP = 5,          /* a HIP runtime call failed                    */
+    HR_ERR_TIMEOUT = 6,      /* a wait for the peer exceeded timeout_us      */
+    HR_ERR_ABORTED = 7       /* hr_channel_abort cancelled waiting kernels   */
+} hr_status;
+
+/* Largest number of contributions hr_reduce_f16 folds in one call. */
+#define HR_MAX_G 16
+
+/* Default cap of one exchange: 131072 binary16 values = 256 KiB per rank,
+ * the payload limit the 1Cat-vLLM page admits to the host path ("Purpose"). */
+#define HR_DEFAULT_MAX_NUMEL 131072u
+
+/* Default watchdog for one wait on the peer, in microseconds. */
+#define HR_DEFAULT_TIMEOUT_US 1000000u
+
+typedef struct {
+    int device;           /* HIP device ordinal the channel's kernels run on  */
+    int world_size;       /* ranks in the group; only 2 is supported          */
+    size_t max_numel;     /* largest numel of one call; 0 = HR_DEFAULT_MAX_NUMEL */
+    int num_blocks;       /* workgroups per rank launch; 0 = automatic.  Both
+                             ranks of a loopback channel run at once on one
+                             GPU, so the value is clamped to half the device's
+                             compute units.                                    */
+    uint32_t timeout_us;  /* watchdog per wait; 0 = HR_DEFAULT_TIMEOUT_US      */
+} hr_channel_config;
+
+/* Read-only description of a channel, for diagnostics and tests. */
+typedef struct {
+    int device;
+    int world_size;
+    size_t max_numel;
+    int num_blocks;
+    int block_threads;            /* threads per workgroup of one launch      */
+    uint32_t timeout_us;
+    void *host_slots;             /* host address of the slot region:
+                                     [2 parity][2 rank][slot_stride] binary16 */
+    size_t slot_stride;           /* elements per slot (>= max_numel)         */
+    volatile uint32_t *host_flags; /* host address of the ready flags:
+                                     flag of (rank r, block b) at index
+                                     (r * num_blocks + b) * flag_stride       */
+    size_t flag_stride;           /* uint32 words between consecutive flags   */
+    volatile uint32_t *host_error; /* sticky asynchronous status word         */
+    volatile uint32_t *host_abort; /* nonzero = cancel waits                  */
+} hr_channel_info;
+
+/*
+ * hr_create_channel -- set up one two-rank exchange group.
+ *
+ * Allocates the channel's pinned, device-mapped, fine-grained host memory
+ * (slots [2 parity][2 rank][max_numel] binary16, per-workgroup ready flags,
+ * the error and abort words) and its device-resident per-workgroup call
+ * counters, and zeroes them.  The slot region has the 2 x world_size x
+ * max_numel shape of the double-buffered workspace that the SGLang page's
+ * "Modifications" section sizes.  Not capturable (it allocates); call it
+ * before any capture.
+ *
+ * cfg:  see hr_channel_config.  *out receives the handle on success and is
+ *       left untouched on failure.
+ * Errors: HR_ERR_INVALID_ARG (null cfg/out, negative or out-of-range
+ *       fields), HR_ERR_UNSUPPORTED (world_size != 2), HR_ERR_HIP.
+ */
+HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out);
+
+/*
+ * hr_allreduce_f16 -- one two-rank all-reduce call of rank `rank`.
+ *
+ * Enqueues exactly one kernel on `stream`.  Its workgroups each own one
+ * contiguous slice of the numel values: they copy the slice of `in` into this
+ * rank's host slot of the current parity, fence at system scope, raise their
+ * ready flag, wait (watchdog-bounded) for the peer's flag of the same call,
+ * read the peer's slice from its host slot and write fl16(x0 + x1) -- rank 0's
+ * value first -- to `out` (1Cat-vLLM page, "Purpose").  Parity comes from a
+ * device-resident per-workgroup call counter, so a replayed graph alternates
+ * slots without host involvement.
+ *
+ * in, out: device binary16 buffers of numel values; out == in is allowed,
+ *          any other overlap is an error.
+ * numel:   0 enqueues nothing; must not exceed the channel's max_numel.
+ * Both ranks must issue the same sequence of numel values.  Rank 0 and rank
+ * 1 must be driven from streams that can run concurrently (two processes, or
+ * two non-blocking streams of one process), each endpoint by one stream at a
+ * time; both launches must be in flight together or the waits time out.
+ *
+ * Errors: HR_ERR_INVALID_ARG, HR_ERR_ALIGNMENT, HR_ERR_TOO_LARGE (the caller
+ * keeps its own collective for larger payloads), HR_ERR_HIP; and the
+ * channel's sticky HR_ERR_TIMEOUT / HR_ERR_ABORTED, in which case nothing is
+ * launched.  A timed-out or aborted kernel leaves `out` unwritten.
+ */
+HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void *in, void *out,
+                                  size_t numel, hr_stream_t stream);
+
+/*
+ * hr_reduce_f16 -- fold G contributions resident in device memory.
+ *
+ * out[i] = left fold of inputs[0][i] .. inputs[G-1][i] with one binary16
+ * rounding per add (the combine defined at the top of this header).  One
+ * kernel launch on `stream`; the G pointers are copied into the launch, so
+ * the `inputs` array may be freed on return.
+ *
+ * inputs: G device pointers, each to numel binary16 values.
+ * G:      1 .. HR_MAX_G (G = 1 copies inputs[0]).
+ * out:    device buffer of numel values; it may equal any input exactly, any
+ *         partial overlap with an input is an error.
+ * numel:  0 enqueues nothing.
+ * Errors: HR_ERR_INVALID_ARG, HR_ERR_ALIGNMENT, HR_ERR_HIP.
+ */
+HR_API hr_status hr_reduce_f16(const void *const *inputs, int G, void *out, size_t numel,
+                               hr_stream_t stream);
+
+/*
+ * hr_channel_status -- the channel's sticky asynchronous status: HR_OK, or
+ * HR_ERR_TIMEOUT / HR_ERR_ABORTED once a kernel has recorded one.  Reads a
+ * host-mapped word; it does not synchronise, so synchronise the rank streams
+ * first to see the outcome of work already enqueued.  Recovery from an error
+ * is hr_destroy followed by hr_create_channel.
+ */
+HR_API hr_status hr_channel_status(hr_channel ch);
+
+/*
+ * hr_channel_abort -- ask every kernel of this channel that is waiting, or
+ * will wait, for its peer to stop: waits end with HR_ERR_ABORTED recorded in
+ * the channel and `out` unwritten.  Host-side store only; returns at once.
+ */
+HR_API hr_status hr_channel_abort(hr_channel ch);
+
+/* hr_channel_get_info -- fill *info with the channel's layout (read-only). */
+HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *info);
+
+/*
+ * hr_destroy -- release the channel.  Destroy any graph that captured calls
+ * on it first, then synchronise both rank streams, then call this; it
+ * synchronises the channel's device before freeing.  NULL is a no-op.
+ */
+HR_API hr_status hr_destroy(hr_channel ch);
+
+/*
+ * hr_loopback_stream_create -- a stream for one rank of a loopback channel.
+ *
+ * The two launches of one exchange call must run at the same time.  The HIP
+ * runtime spreads ordinary streams over a small pool of hardware queues
+ * (GPU_MAX_HW_QUEUES), and two streams that share a queue run their kernels
+ * one after the other, so ordinary streams give no such guarantee.  A stream
+ * created here owns its hardware queue: it is created with an explicit
+ * compute-unit mask (the runtime never pools such queues) that enables every
+ * compute unit of `device`.  It is ordered with the null stream like any
+ * stream created without hipStreamNonBlocking, so do not enqueue work on the
+ * null stream between the two ranks' launches of one call.
+ *
+ * device: HIP device ordinal.  *out receives a hipStream_t owned by the
+ * caller, released with hr_loopback_stream_destroy.
+ * Errors: HR_ERR_INVALID_ARG, HR_ERR_HIP.
+ */
+HR_API hr_status hr_loopback_stream_create(int device, hr_stream_t *out);
+
+/* hr_loopback_stream_destroy -- release a stream from
+ * hr_loopback_stream_create (after its work has finished).  NULL is a no-op. */
+HR_API hr_status hr_loopback_stream_destroy(hr_stream_t stream);
+
+/* Static, human-readable name of a status code. */
+HR_API const char *hr_status_str(hr_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HR_H */

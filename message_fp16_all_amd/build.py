@@ -1,0 +1,49 @@
+"""Build ``libhr.so`` (the C-ABI library and its gfx950 kernels) in-tree.
+
+Run ``python -m message_fp16_all_amd.build`` or call ``build()``.  The
+library is compiled by hipcc for gfx950 only, without fast-math, and with
+packed FP32 instruction selection switched off (the kernels do binary16
+arithmetic; nothing in them wants packed FP32).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libhr.so")
+SOURCES = [os.path.join(CSRC, f) for f in ("fold.hip", "exchange.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-fvisibility=hidden",
+    "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE,
+    "-Wl,-rpath,/opt/rocm/lib",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into ``message_fp16_all_amd/libhr.so``."""
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

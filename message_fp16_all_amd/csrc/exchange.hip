@@ -1,0 +1,394 @@
+// exchange.hip -- the two-rank FP16 all-reduce through pinned host slots.
+//
+// The method is the one the 1Cat-vLLM pull request "[Kernel] Two-rank FP16
+// all-reduce through pinned host memory for GPUs without P2P" lays out in
+// its "Purpose" section: one kernel per call; each workgroup writes its chunk
+// of the rank's contribution into host memory that both ranks map, fences,
+// raises a per-workgroup ready flag, waits for the peer's flag and adds the
+// peer's chunk with a single FP16 rounding, so both ranks obtain the same
+// bits; there is no CPU work and no stream synchronisation, so the call can
+// be captured into a graph, and the host slots are double buffered by call
+// parity.  Channels are handles so one process can own several groups (same
+// section).
+//
+// Channel memory
+//   host (pinned, device-mapped, fine-grained/coherent):
+//     slots  [2 parity][2 rank][stride] binary16
+//     flags  [2 rank][nblocks], one 128-byte line each: the call number of
+//            the last chunk that workgroup published
+//     error word, abort word (one line each)
+//   device (HBM): epoch[2 rank][nblocks] -- per-workgroup call counter,
+//     device error word.
+//
+// Call protocol of workgroup b of rank r at call e (= its counter + 1):
+//   1. load its slice of `in` and store it to slot[e & 1][r]        (D2H)
+//   2. every lane: system-scope fence; barrier; lane 0: release-store
+//      flag[r][b] = e at system scope
+//   3. lane 0 polls flag[peer][b] with system-scope acquire loads until it
+//      reaches e (wrap-safe signed compare, so a peer already at e + 1 also
+//      releases the wait), sleeping between polls; it also polls the abort
+//      word and a watchdog on the constant-rate wall clock
+//   4. barrier, acquire fence, load slot[e & 1][peer] (H2D) and its own
+//      slice of `in` again, store fl16(x0 + x1) with rank 0's value first
+//      to `out`.
+// Why one parity cannot be overwritten while the peer still reads it: a
+// rank's workgroup publishes call e + 2 (same parity as e) only after its
+// wait in call e + 1 saw the peer's flag of call e + 1, which the peer raises
+// only after its whole call-e kernel has finished (stream order).
+//
+// Errors (timeout, abort) are written to the device error word and the
+// host-mapped error word; a kernel that finds the device word set returns at
+// once without touching `out`, so a failed call cannot cascade into a long
+// chain of timeouts inside a replayed graph.
+#include "hr_internal.h"
+
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+namespace hr {
+
+constexpr int kExchThreads = 256;
+constexpr int kExchUnroll = 4;
+constexpr size_t kLine = 128;                     // bytes per flag / word line
+constexpr size_t kFlagStride = kLine / sizeof(uint32_t);
+
+struct ExchArgs {
+    const void *in;
+    void *out;
+    size_t numel;
+    uint16_t *slots;          // device view of the host slot region
+    size_t stride;            // values per slot
+    uint32_t *flags;          // device view of the host flags
+    uint32_t *epochs;         // this rank's counters (HBM)
+    uint32_t *dev_error;      // HBM
+    uint32_t *host_error;     // device view of the host error word
+    const uint32_t *abort_w;  // device view of the host abort word
+    uint64_t timeout_ticks;
+    int rank;
+    int nblocks;
+};
+
+__device__ __forceinline__ u32x4 combine(u32x4 x0, u32x4 x1) { return add_f16x8(x0, x1); }
+__device__ __forceinline__ uint16_t combine(uint16_t x0, uint16_t x1) { return add_f16x1(x0, x1); }
+
+// T is the unit of one lane access: u32x4 (8 values, 16-byte aligned
+// buffers) or uint16_t (1 value, any 2-byte aligned buffers).
+template <typename T>
+__global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
+    __shared__ uint32_t s_epoch;
+    __shared__ uint32_t s_status;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+
+    if (tid == 0) {
+        const uint32_t err = __hip_atomic_load(a.dev_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t e = __hip_atomic_load(&a.epochs[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        if (err == 0) __hip_atomic_store(&a.epochs[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_epoch = e;
+        s_status = err;
+    }
+    __syncthreads();
+    if (s_status != 0) return;
+    const uint32_t e = s_epoch;
+    const int parity = static_cast<int>(e & 1u);
+    const int peer = a.rank ^ 1;
+
+    constexpr size_t per = sizeof(T) / sizeof(uint16_t);
+    const size_t nunits = a.numel / per;
+    const size_t lo = nunits * static_cast<size_t>(b) / static_cast<size_t>(a.nblocks);
+    const size_t hi = nunits * static_cast<size_t>(b + 1) / static_cast<size_t>(a.nblocks);
+    const bool last = (b == a.nblocks - 1);
+    const size_t tail0 = nunits * per;  // first value not covered by whole units
+
+    const T *in = static_cast<const T *>(a.in);
+    T *out = static_cast<T *>(a.out);
+    T *mine = reinterpret_cast<T *>(a.slots + (static_cast<size_t>(2 * parity + a.rank)) * a.stride);
+    const T *theirs = reinterpret_cast<const T *>(a.slots + (static_cast<size_t>(2 * parity + peer)) * a.stride);
+
+    // 1. publish this rank's slice into its host slot
+    for (size_t v0 = lo + tid; v0 < hi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
+        T x[kExchUnroll];
+#pragma unroll
+        for (int u = 0; u < kExchUnroll; ++u) {
+            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+            if (v < hi) x[u] = in[v];
+        }
+#pragma unroll
+        for (int u = 0; u < kExchUnroll; ++u) {
+            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+            if (v < hi) mine[v] = x[u];
+        }
+    }
+    if (last && tail0 + tid < a.numel) {
+        const uint16_t *in16 = static_cast<const uint16_t *>(a.in);
+        uint16_t *mine16 = a.slots + (static_cast<size_t>(2 * parity + a.rank)) * a.stride;
+        mine16[tail0 + tid] = in16[tail0 + tid];
+    }
+
+    // 2. every lane's slot stores are visible system-wide before the flag
+    __threadfence_system();
+    __syncthreads();
+
+    // 3. raise this workgroup's flag, then wait for the peer's
+    if (tid == 0) {
+        __hip_atomic_store(a.flags + (static_cast<size_t>(a.rank) * a.nblocks + b) * kFlagStride, e,
+                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        const uint32_t *pf = a.flags + (static_cast<size_t>(peer) * a.nblocks + b) * kFlagStride;
+        uint32_t status = 0;
+        const long long t0 = wall_clock64();
+        for (;;) {
+            const uint32_t f = __hip_atomic_load(pf, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (static_cast<int32_t>(f - e) >= 0) break;
+            if (__hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) {
+                status = HR_ERR_ABORTED;
+                break;
+            }
+            if (static_cast<uint64_t>(wall_clock64() - t0) > a.timeout_ticks) {
+                status = HR_ERR_TIMEOUT;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (status != 0) {
+            __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.host_error, status, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        s_status = status;
+    }
+    __syncthreads();
+    if (s_status != 0) return;
+    // order every lane's slot loads after the flag observed by lane 0
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+
+    // 4. combine in rank order: x0 + x1
+    for (size_t v0 = lo + tid; v0 < hi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
+        T y[kExchUnroll], x[kExchUnroll];
+#pragma unroll
+        for (int u = 0; u < kExchUnroll; ++u) {
+            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+            if (v < hi) {
+                y[u] = theirs[v];
+                x[u] = in[v];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kExchUnroll; ++u) {
+            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+            if (v < hi) out[v] = (a.rank == 0) ? combine(x[u], y[u]) : combine(y[u], x[u]);
+        }
+    }
+    if (last && tail0 + tid < a.numel) {
+        const uint16_t *in16 = static_cast<const uint16_t *>(a.in);
+        const uint16_t *theirs16 = a.slots + (static_cast<size_t>(2 * parity + peer)) * a.stride;
+        const uint16_t xv = in16[tail0 + tid], yv = theirs16[tail0 + tid];
+        static_cast<uint16_t *>(a.out)[tail0 + tid] = (a.rank == 0) ? add_f16x1(xv, yv) : add_f16x1(yv, xv);
+    }
+}
+
+}  // namespace hr
+
+using namespace hr;
+
+struct hr_channel_s {
+    int device;
+    int world_size;
+    size_t max_numel;
+    size_t stride;
+    int nblocks;
+    uint32_t timeout_us;
+    uint64_t timeout_ticks;
+    void *host_base;           // hipHostMalloc'ed region (host address)
+    unsigned char *host_dev;   // the same region as seen by the device
+    size_t flags_off, error_off, abort_off, host_bytes;
+    uint32_t *dev_words;       // hipMalloc: epochs[2 * nblocks] then the error word
+};
+
+namespace {
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) return;
+        ok = (prev == dev) || (hipSetDevice(dev) == hipSuccess);
+    }
+    ~DeviceGuard() {
+        if (ok && prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+void release(hr_channel ch) {
+    if (ch->host_base) (void)hipHostFree(ch->host_base);
+    if (ch->dev_words) (void)hipFree(ch->dev_words);
+    delete ch;
+}
+
+}  // namespace
+
+extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out) {
+    if (cfg == nullptr || out == nullptr) return HR_ERR_INVALID_ARG;
+    if (cfg->world_size != 2) return HR_ERR_UNSUPPORTED;
+    if (cfg->device < 0 || cfg->num_blocks < 0) return HR_ERR_INVALID_ARG;
+    const size_t max_numel = cfg->max_numel ? cfg->max_numel : HR_DEFAULT_MAX_NUMEL;
+    if (max_numel > (size_t(1) << 30)) return HR_ERR_INVALID_ARG;  // 2 GiB of slots per rank
+    const uint32_t timeout_us = cfg->timeout_us ? cfg->timeout_us : HR_DEFAULT_TIMEOUT_US;
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess) return HR_ERR_HIP;
+    if (cfg->device >= ndev) return HR_ERR_INVALID_ARG;
+    DeviceGuard guard(cfg->device);
+    if (!guard.ok) return HR_ERR_HIP;
+
+    int cus = 0, clock_khz = 0;
+    if (device_cu_count(cfg->device, &cus) != hipSuccess) return HR_ERR_HIP;
+    if (hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, cfg->device) != hipSuccess ||
+        clock_khz <= 0)
+        return HR_ERR_UNSUPPORTED;
+
+    hr_channel ch = new (std::nothrow) hr_channel_s{};
+    if (ch == nullptr) return HR_ERR_HIP;
+    ch->device = cfg->device;
+    ch->world_size = 2;
+    ch->max_numel = max_numel;
+    ch->stride = round_up(max_numel, kLine / sizeof(uint16_t));
+    // Default: half of the compute units per rank, so that both ranks of a
+    // loopback channel are resident at once.
+    int nb = cfg->num_blocks ? cfg->num_blocks : cus / 2;
+    if (nb > cus / 2) nb = cus / 2;
+    if (nb < 1) nb = 1;
+    ch->nblocks = nb;
+    ch->timeout_us = timeout_us;
+    ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
+
+    const size_t slot_bytes = 4 * ch->stride * sizeof(uint16_t);
+    ch->flags_off = round_up(slot_bytes, kLine);
+    ch->error_off = ch->flags_off + 2 * static_cast<size_t>(nb) * kLine;
+    ch->abort_off = ch->error_off + kLine;
+    ch->host_bytes = ch->abort_off + kLine;
+
+    void *dev_view = nullptr;
+    if (hipHostMalloc(&ch->host_base, ch->host_bytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
+        hipHostGetDevicePointer(&dev_view, ch->host_base, 0) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&ch->dev_words), (2 * static_cast<size_t>(nb) + 1) * sizeof(uint32_t)) !=
+            hipSuccess ||
+        hipMemset(ch->dev_words, 0, (2 * static_cast<size_t>(nb) + 1) * sizeof(uint32_t)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        release(ch);
+        return HR_ERR_HIP;
+    }
+    ch->host_dev = static_cast<unsigned char *>(dev_view);
+    std::memset(ch->host_base, 0, ch->host_bytes);
+    __atomic_thread_fence(__ATOMIC_SEQ_CST);
+    *out = ch;
+    return HR_OK;
+}
+
+extern "C" HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void *in, void *out, size_t numel,
+                                             hr_stream_t stream) {
+    if (ch == nullptr || (rank != 0 && rank != 1)) return HR_ERR_INVALID_ARG;
+    const uint32_t sticky = __atomic_load_n(
+        reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->error_off), __ATOMIC_ACQUIRE);
+    if (sticky != 0) return static_cast<hr_status>(sticky);
+    if (numel == 0) return HR_OK;
+    if (in == nullptr || out == nullptr) return HR_ERR_INVALID_ARG;
+    if (numel > ch->max_numel) return HR_ERR_TOO_LARGE;
+    if (!aligned(in, 2) || !aligned(out, 2)) return HR_ERR_ALIGNMENT;
+    if (partial_overlap(in, out, numel * 2)) return HR_ERR_INVALID_ARG;
+
+    int dev = -1;
+    if (stream_device(stream, &dev) != hipSuccess) return HR_ERR_HIP;
+    if (dev != ch->device) return HR_ERR_INVALID_ARG;
+
+    ExchArgs a{};
+    a.in = in;
+    a.out = out;
+    a.numel = numel;
+    a.slots = reinterpret_cast<uint16_t *>(ch->host_dev);
+    a.stride = ch->stride;
+    a.flags = reinterpret_cast<uint32_t *>(ch->host_dev + ch->flags_off);
+    a.epochs = ch->dev_words + static_cast<size_t>(rank) * ch->nblocks;
+    a.dev_error = ch->dev_words + 2 * static_cast<size_t>(ch->nblocks);
+    a.host_error = reinterpret_cast<uint32_t *>(ch->host_dev + ch->error_off);
+    a.abort_w = reinterpret_cast<const uint32_t *>(ch->host_dev + ch->abort_off);
+    a.timeout_ticks = ch->timeout_ticks;
+    a.rank = rank;
+    a.nblocks = ch->nblocks;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (aligned(in, 16) && aligned(out, 16))
+        hipLaunchKernelGGL(exchange_f16<u32x4>, dim3(ch->nblocks), dim3(kExchThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(exchange_f16<uint16_t>, dim3(ch->nblocks), dim3(kExchThreads), 0, s, a);
+    return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
+}
+
+extern "C" HR_API hr_status hr_channel_status(hr_channel ch) {
+    if (ch == nullptr) return HR_ERR_INVALID_ARG;
+    return static_cast<hr_status>(__atomic_load_n(
+        reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->error_off), __ATOMIC_ACQUIRE));
+}
+
+extern "C" HR_API hr_status hr_channel_abort(hr_channel ch) {
+    if (ch == nullptr) return HR_ERR_INVALID_ARG;
+    __atomic_store_n(reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->abort_off), 1u,
+                     __ATOMIC_RELEASE);
+    __atomic_thread_fence(__ATOMIC_SEQ_CST);
+    return HR_OK;
+}
+
+extern "C" HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *info) {
+    if (ch == nullptr || info == nullptr) return HR_ERR_INVALID_ARG;
+    unsigned char *base = static_cast<unsigned char *>(ch->host_base);
+    info->device = ch->device;
+    info->world_size = ch->world_size;
+    info->max_numel = ch->max_numel;
+    info->num_blocks = ch->nblocks;
+    info->block_threads = kExchThreads;
+    info->timeout_us = ch->timeout_us;
+    info->host_slots = base;
+    info->slot_stride = ch->stride;
+    info->host_flags = reinterpret_cast<volatile uint32_t *>(base + ch->flags_off);
+    info->flag_stride = kFlagStride;
+    info->host_error = reinterpret_cast<volatile uint32_t *>(base + ch->error_off);
+    info->host_abort = reinterpret_cast<volatile uint32_t *>(base + ch->abort_off);
+    return HR_OK;
+}
+
+extern "C" HR_API hr_status hr_destroy(hr_channel ch) {
+    if (ch == nullptr) return HR_OK;
+    hr_status st = HR_OK;
+    {
+        DeviceGuard guard(ch->device);
+        if (!guard.ok || hipDeviceSynchronize() != hipSuccess) st = HR_ERR_HIP;
+    }
+    release(ch);
+    return st;
+}
+
+extern "C" HR_API hr_status hr_loopback_stream_create(int device, hr_stream_t *out) {
+    if (out == nullptr || device < 0) return HR_ERR_INVALID_ARG;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess) return HR_ERR_HIP;
+    if (device >= ndev) return HR_ERR_INVALID_ARG;
+    DeviceGuard guard(device);
+    if (!guard.ok) return HR_ERR_HIP;
+    int cus = 0;
+    if (device_cu_count(device, &cus) != hipSuccess) return HR_ERR_HIP;
+    // every compute unit enabled: the mask only buys a dedicated queue
+    std::vector<uint32_t> mask((static_cast<size_t>(cus) + 31) / 32, 0u);
+    for (int i = 0; i < cus; ++i) mask[static_cast<size_t>(i) / 32] |= 1u << (i % 32);
+    hipStream_t s = nullptr;
+    if (hipExtStreamCreateWithCUMask(&s, static_cast<uint32_t>(mask.size()), mask.data()) != hipSuccess)
+        return HR_ERR_HIP;
+    *out = reinterpret_cast<hr_stream_t>(s);
+    return HR_OK;
+}
+
+extern "C" HR_API hr_status hr_loopback_stream_destroy(hr_stream_t stream) {
+    if (stream == nullptr) return HR_OK;
+    return hipStreamDestroy(reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? HR_OK : HR_ERR_HIP;
+}

@@ -1,0 +1,259 @@
+"""Python binding of libhr (``include/hr.h``): argument marshalling only.
+
+Every function named ``hr_*`` here calls the C entry point of the same name
+with the same arguments; every step of the combine runs in libhr's HIP
+kernels.  The torch helpers at the bottom only turn tensors and streams into
+the device pointers and ``hipStream_t`` handles those entry points take:
+PyTorch is used for device memory and streams, nothing else.
+
+The library is loaded from this package's directory on first use.  If it is
+missing, loading raises ``ImportError``: there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhr.so")
+
+HR_OK = 0
+HR_ERR_INVALID_ARG = 1
+HR_ERR_ALIGNMENT = 2
+HR_ERR_TOO_LARGE = 3
+HR_ERR_UNSUPPORTED = 4
+HR_ERR_HIP = 5
+HR_ERR_TIMEOUT = 6
+HR_ERR_ABORTED = 7
+
+HR_MAX_G = 16
+HR_DEFAULT_MAX_NUMEL = 131072
+HR_DEFAULT_TIMEOUT_US = 1_000_000
+
+# Every symbol include/hr.h declares.
+EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel_status",
+           "hr_channel_abort", "hr_channel_get_info", "hr_destroy", "hr_status_str",
+           "hr_loopback_stream_create", "hr_loopback_stream_destroy")
+
+
+class hr_channel_config(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_int),
+                ("world_size", ctypes.c_int),
+                ("max_numel", ctypes.c_size_t),
+                ("num_blocks", ctypes.c_int),
+                ("timeout_us", ctypes.c_uint32)]
+
+
+class hr_channel_info(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_int),
+                ("world_size", ctypes.c_int),
+                ("max_numel", ctypes.c_size_t),
+                ("num_blocks", ctypes.c_int),
+                ("block_threads", ctypes.c_int),
+                ("timeout_us", ctypes.c_uint32),
+                ("host_slots", ctypes.c_void_p),
+                ("slot_stride", ctypes.c_size_t),
+                ("host_flags", ctypes.POINTER(ctypes.c_uint32)),
+                ("flag_stride", ctypes.c_size_t),
+                ("host_error", ctypes.POINTER(ctypes.c_uint32)),
+                ("host_abort", ctypes.POINTER(ctypes.c_uint32))]
+
+
+class HrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {hr_status_str(status)} ({status})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libhr.so from this package (raises ImportError if it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m message_fp16_all_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.hr_create_channel.argtypes = [ctypes.POINTER(hr_channel_config), ctypes.POINTER(vp)]
+    lib.hr_allreduce_f16.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+    lib.hr_reduce_f16.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.hr_channel_status.argtypes = [vp]
+    lib.hr_channel_abort.argtypes = [vp]
+    lib.hr_channel_get_info.argtypes = [vp, ctypes.POINTER(hr_channel_info)]
+    lib.hr_destroy.argtypes = [vp]
+    lib.hr_loopback_stream_create.argtypes = [ctypes.c_int, ctypes.POINTER(vp)]
+    lib.hr_loopback_stream_destroy.argtypes = [vp]
+    lib.hr_status_str.argtypes = [ctypes.c_int]
+    lib.hr_status_str.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name != "hr_status_str":
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------- the C entry points
+
+def hr_status_str(status: int) -> str:
+    return load().hr_status_str(int(status)).decode()
+
+
+def hr_create_channel(device: int = 0, world_size: int = 2, max_numel: int = 0,
+                      num_blocks: int = 0, timeout_us: int = 0) -> int:
+    """Returns the channel handle (an integer address) or raises HrError."""
+    cfg = hr_channel_config(device, world_size, max_numel, num_blocks, timeout_us)
+    h = ctypes.c_void_p()
+    st = load().hr_create_channel(ctypes.byref(cfg), ctypes.byref(h))
+    if st != HR_OK:
+        raise HrError(st, "hr_create_channel")
+    return h.value
+
+
+def hr_allreduce_f16(ch: int, rank: int, in_ptr: int, out_ptr: int, numel: int,
+                     stream: int) -> int:
+    """Raw call; returns the hr_status code."""
+    return load().hr_allreduce_f16(ch, rank, in_ptr, out_ptr, numel, stream)
+
+
+def hr_reduce_f16(ptrs, G: int, out_ptr: int, numel: int, stream: int) -> int:
+    """Raw call; ``ptrs`` is a sequence of G device addresses.  Returns hr_status."""
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    return load().hr_reduce_f16(arr, G, out_ptr, numel, stream)
+
+
+def hr_channel_status(ch: int) -> int:
+    return load().hr_channel_status(ch)
+
+
+def hr_channel_abort(ch: int) -> int:
+    return load().hr_channel_abort(ch)
+
+
+def hr_channel_get_info(ch: int) -> hr_channel_info:
+    info = hr_channel_info()
+    st = load().hr_channel_get_info(ch, ctypes.byref(info))
+    if st != HR_OK:
+        raise HrError(st, "hr_channel_get_info")
+    return info
+
+
+def hr_destroy(ch: int) -> int:
+    return load().hr_destroy(ch)
+
+
+def hr_loopback_stream_create(device: int = 0) -> int:
+    """Returns a hipStream_t (integer) that owns its hardware queue."""
+    h = ctypes.c_void_p()
+    st = load().hr_loopback_stream_create(device, ctypes.byref(h))
+    if st != HR_OK:
+        raise HrError(st, "hr_loopback_stream_create")
+    return h.value
+
+
+def hr_loopback_stream_destroy(stream: int) -> int:
+    return load().hr_loopback_stream_destroy(stream)
+
+
+# ----------------------------------------------------- torch marshalling
+
+def _check(st: int, where: str):
+    if st != HR_OK:
+        raise HrError(st, where)
+
+
+def _f16_ptr(t, name: str) -> int:
+    import torch
+    if t.dtype != torch.float16:
+        raise TypeError(f"{name}: expected torch.float16, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def reduce(tensors, out, stream=None):
+    """out = left fold of ``tensors`` (torch.float16, same numel) on ``stream``."""
+    n = out.numel()
+    ptrs = []
+    for i, t in enumerate(tensors):
+        if t.numel() != n:
+            raise ValueError(f"tensors[{i}] has {t.numel()} values, out has {n}")
+        ptrs.append(_f16_ptr(t, f"tensors[{i}]"))
+    _check(hr_reduce_f16(ptrs, len(ptrs), _f16_ptr(out, "out"), n, _stream_handle(stream)),
+           "hr_reduce_f16")
+    return out
+
+
+class Channel:
+    """An owned two-rank channel; ``allreduce`` enqueues one rank's call."""
+
+    def __init__(self, device: int = 0, max_numel: int = 0, num_blocks: int = 0,
+                 timeout_us: int = 0):
+        self.handle = hr_create_channel(device, 2, max_numel, num_blocks, timeout_us)
+
+    def allreduce(self, rank: int, inp, out, stream=None):
+        n = inp.numel()
+        if out.numel() != n:
+            raise ValueError("in and out differ in numel")
+        _check(hr_allreduce_f16(self.handle, rank, _f16_ptr(inp, "in"), _f16_ptr(out, "out"), n,
+                                _stream_handle(stream)), "hr_allreduce_f16")
+        return out
+
+    def status(self) -> int:
+        return hr_channel_status(self.handle)
+
+    def abort(self):
+        _check(hr_channel_abort(self.handle), "hr_channel_abort")
+
+    def info(self) -> hr_channel_info:
+        return hr_channel_get_info(self.handle)
+
+    def destroy(self):
+        if self.handle:
+            st = hr_destroy(self.handle)
+            self.handle = None
+            _check(st, "hr_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.destroy()
+
+
+class LoopbackStreams:
+    """Two streams for the two ranks of a loopback channel, each owning its
+    hardware queue (see hr_loopback_stream_create), wrapped as torch streams."""
+
+    def __init__(self, device: int = 0):
+        import torch
+        self.handles = [hr_loopback_stream_create(device), hr_loopback_stream_create(device)]
+        self.streams = tuple(torch.cuda.ExternalStream(h, device=torch.device("cuda", device))
+                             for h in self.handles)
+
+    def __getitem__(self, i):
+        return self.streams[i]
+
+    def __iter__(self):
+        return iter(self.streams)
+
+    def __len__(self):
+        return 2
+
+    def destroy(self):
+        for s in self.streams:
+            s.synchronize()
+        for h in self.handles:
+            _check(hr_loopback_stream_destroy(h), "hr_loopback_stream_destroy")
+        self.handles = []

@@ -1,0 +1,328 @@
+"""GPU parity of hr_allreduce_f16: the two-rank exchange through host slots.
+
+Both ranks run on one GPU as two concurrently resident launches on two
+streams that each own a hardware queue (loopback).  Every output value of both ranks is
+compared bit for bit (NaN by class) with the oracle's single-rounding sum of
+the two contributions, and the two ranks' outputs with each other.
+"""
+import ctypes
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from message_fp16_all_amd import hr, inputs
+from _gpu import assert_same_bits, needs_gpu, specials_mix, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+TIMEOUT_US = 2_000_000
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture
+def streams():
+    # one dedicated hardware queue per rank, so the two launches of a call
+    # always run at the same time
+    ls = hr.LoopbackStreams(0)
+    yield ls
+    ls.destroy()
+
+
+@pytest.fixture
+def channel():
+    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=TIMEOUT_US)
+    yield ch
+    torch.cuda.synchronize()
+    ch.destroy()
+
+
+def loopback(ch, x0, x1, out0, out1, streams):
+    s0, s1 = streams
+    torch.cuda.synchronize()
+    ch.allreduce(0, x0, out0, s0)
+    ch.allreduce(1, x1, out1, s1)
+    s0.synchronize()
+    s1.synchronize()
+    assert ch.status() == hr.HR_OK, hr.hr_status_str(ch.status())
+
+
+def check_pair(out0, out1, x0_bits, x1_bits, what):
+    ref = oracle.add(x0_bits, x1_bits)
+    g0, g1 = to_host(out0), to_host(out1)
+    assert_same_bits(g0, ref, f"{what} rank 0")
+    assert_same_bits(g1, ref, f"{what} rank 1")
+    assert np.array_equal(g0, g1), f"{what}: ranks differ"
+
+
+@pytest.mark.parametrize("tokens", inputs.TOKENS_EXCHANGE)
+def test_workload2_loopback(channel, streams, tokens):
+    x0b, x1b = inputs.workload2(tokens)
+    say(f"exchange: workload 2, tokens={tokens} N={x0b.size}")
+    x0, x1 = to_dev(x0b), to_dev(x1b)
+    out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+    loopback(channel, x0, x1, out0, out1, streams)
+    check_pair(out0, out1, x0b, x1b, f"tokens {tokens}")
+
+
+def test_edge_table_through_the_exchange(channel, streams):
+    a, b = inputs.edge_pairs()
+    x0, x1 = to_dev(a), to_dev(b)
+    out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+    loopback(channel, x0, x1, out0, out1, streams)
+    ref = oracle.add(a, b)
+    assert_same_bits(to_host(out0), ref, "edge rank 0")
+    assert_same_bits(to_host(out1), ref, "edge rank 1")
+
+
+def test_consecutive_calls_alternate_parity_with_varying_sizes(channel, streams):
+    sizes = [4096, 131_072, 1, 65_541, 8, 9, 131_072, 32_768, 7, 100_000, 4096, 2]
+    for call, n in enumerate(sizes):
+        x0b = specials_mix(n, seed=10 * call)
+        x1b = specials_mix(n, seed=10 * call + 1)
+        x0, x1 = to_dev(x0b), to_dev(x1b)
+        out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+        loopback(channel, x0, x1, out0, out1, streams)
+        check_pair(out0, out1, x0b, x1b, f"call {call} n={n}")
+
+
+def test_back_to_back_calls_without_host_sync(channel, streams):
+    """Many calls queued at once on both streams: the slot parity alternates
+    on the device while the host never waits between calls."""
+    s0, s1 = streams
+    calls, n = 64, 16_384
+    x = [[inputs.gaussian(n, 1.0, 20, r, c) for c in range(calls)] for r in range(2)]
+    xin = [torch.stack([to_dev(v) for v in x[r]]) for r in range(2)]
+    outs = [torch.empty_like(xin[r]) for r in range(2)]
+    torch.cuda.synchronize()
+    for c in range(calls):
+        channel.allreduce(0, xin[0][c], outs[0][c], s0)
+        channel.allreduce(1, xin[1][c], outs[1][c], s1)
+    s0.synchronize()
+    s1.synchronize()
+    assert channel.status() == hr.HR_OK
+    for c in range(calls):
+        check_pair(outs[0][c], outs[1][c], x[0][c], x[1][c], f"call {c}")
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 4097, 131_071, 131_072])
+def test_ragged_sizes(channel, streams, n):
+    x0b, x1b = specials_mix(n, seed=n), specials_mix(n, seed=n + 1)
+    x0, x1 = to_dev(x0b), to_dev(x1b)
+    out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+    loopback(channel, x0, x1, out0, out1, streams)
+    check_pair(out0, out1, x0b, x1b, f"n={n}")
+
+
+@pytest.mark.parametrize("offset", [1, 3])
+def test_unaligned_buffers(channel, streams, offset):
+    n = 20_000
+    x0b, x1b = specials_mix(n, 5), specials_mix(n, 6)
+    pad = np.zeros(offset, np.uint16)
+    b0, b1 = to_dev(np.concatenate([pad, x0b])), to_dev(np.concatenate([pad, x1b]))
+    o0 = torch.zeros(n + offset, dtype=torch.float16, device="cuda:0")
+    o1 = torch.zeros(n + offset, dtype=torch.float16, device="cuda:0")
+    loopback(channel, b0[offset:], b1[offset:], o0[offset:], o1[offset:], streams)
+    check_pair(o0[offset:], o1[offset:], x0b, x1b, f"offset {offset}")
+    assert np.all(to_host(o0[:offset]) == 0) and np.all(to_host(o1[:offset]) == 0)
+
+
+def test_in_place(channel, streams):
+    n = 131_072
+    x0b, x1b = inputs.workload2(32, call=7)
+    x0, x1 = to_dev(x0b), to_dev(x1b)
+    loopback(channel, x0, x1, x0, x1, streams)
+    check_pair(x0, x1, x0b, x1b, "in place")
+
+
+def test_too_large_is_refused_and_channel_stays_usable(channel, streams):
+    n = hr.HR_DEFAULT_MAX_NUMEL + 1
+    x = torch.zeros(n, dtype=torch.float16, device="cuda:0")
+    with pytest.raises(hr.HrError) as ei:
+        channel.allreduce(0, x, x, streams[0])
+    assert ei.value.status == hr.HR_ERR_TOO_LARGE
+    x0b, x1b = inputs.workload2(1)
+    x0, x1 = to_dev(x0b), to_dev(x1b)
+    out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+    loopback(channel, x0, x1, out0, out1, streams)
+    check_pair(out0, out1, x0b, x1b, "after refusal")
+
+
+@pytest.mark.parametrize("first", [0, 1])
+def test_skewed_arrival(channel, streams, first):
+    """One rank arrives 30 ms after the other; the early one waits."""
+    x0b, x1b = inputs.workload2(8, call=3)
+    x = [to_dev(x0b), to_dev(x1b)]
+    out = [torch.empty_like(x[0]), torch.empty_like(x[1])]
+    torch.cuda.synchronize()
+    channel.allreduce(first, x[first], out[first], streams[first])
+    time.sleep(0.03)
+    other = first ^ 1
+    channel.allreduce(other, x[other], out[other], streams[other])
+    streams[0].synchronize()
+    streams[1].synchronize()
+    assert channel.status() == hr.HR_OK
+    check_pair(out[0], out[1], x0b, x1b, f"skew first={first}")
+
+
+def test_peer_never_arrives_times_out(streams):
+    ch = hr.Channel(timeout_us=20_000)
+    try:
+        x = to_dev(inputs.workload2(4)[0])
+        out = torch.full_like(x, 3.0)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        ch.allreduce(0, x, out, streams[0])
+        streams[0].synchronize()
+        dt = time.time() - t0
+        assert ch.status() == hr.HR_ERR_TIMEOUT
+        assert dt < 5.0
+        # the timed-out kernel left out unwritten
+        assert torch.all(out == 3.0)
+        # sticky: the next call is refused without a launch
+        with pytest.raises(hr.HrError) as ei:
+            ch.allreduce(1, x, out, streams[1])
+        assert ei.value.status == hr.HR_ERR_TIMEOUT
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+
+
+def test_abort_releases_a_waiting_kernel(streams):
+    ch = hr.Channel(timeout_us=5_000_000)
+    try:
+        x = to_dev(inputs.workload2(4)[0])
+        out = torch.full_like(x, 3.0)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        ch.allreduce(0, x, out, streams[0])
+        time.sleep(0.05)
+        ch.abort()
+        streams[0].synchronize()
+        dt = time.time() - t0
+        assert ch.status() == hr.HR_ERR_ABORTED
+        assert dt < 2.5, dt
+        assert torch.all(out == 3.0)
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+
+
+def test_host_acts_as_the_peer(streams):
+    """Integrity of both directions of the host link: the kernel's slot writes
+    are read back by the CPU bit for bit, and values the CPU writes into the
+    peer's slot (then flags) are what the kernel adds."""
+    ch = hr.Channel(timeout_us=TIMEOUT_US)
+    try:
+        info = ch.info()
+        n = 65_536 + 3
+        x0b, x1b = specials_mix(n, 41), specials_mix(n, 42)
+        x0 = to_dev(x0b)
+        out0 = torch.empty_like(x0)
+        torch.cuda.synchronize()
+        ch.allreduce(0, x0, out0, streams[0])          # call 1 -> parity 1
+        stride_bytes = info.slot_stride * 2
+        peer_slot = info.host_slots + (2 * 1 + 1) * stride_bytes
+        own_slot = info.host_slots + (2 * 1 + 0) * stride_bytes
+        ctypes.memmove(peer_slot, x1b.ctypes.data, n * 2)
+        for b in range(info.num_blocks):
+            info.host_flags[(1 * info.num_blocks + b) * info.flag_stride] = 1
+        streams[0].synchronize()
+        assert ch.status() == hr.HR_OK
+        assert_same_bits(to_host(out0), oracle.add(x0b, x1b), "host peer")
+        seen = np.frombuffer(ctypes.string_at(own_slot, n * 2), dtype=np.uint16)
+        assert np.array_equal(seen, x0b)
+        for b in range(info.num_blocks):
+            assert info.host_flags[(0 * info.num_blocks + b) * info.flag_stride] == 1
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+
+
+def test_two_channels_in_one_process(streams):
+    chs = [hr.Channel(max_numel=32_768, timeout_us=TIMEOUT_US),
+           hr.Channel(max_numel=32_768, num_blocks=16, timeout_us=TIMEOUT_US)]
+    try:
+        for call in range(6):
+            ch = chs[call % 2]
+            x0b, x1b = inputs.gaussian(32_768, 1, 30, 0, call), inputs.gaussian(32_768, 1, 30, 1, call)
+            x0, x1 = to_dev(x0b), to_dev(x1b)
+            out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+            loopback(ch, x0, x1, out0, out1, streams)
+            check_pair(out0, out1, x0b, x1b, f"channel {call % 2} call {call}")
+    finally:
+        torch.cuda.synchronize()
+        for ch in chs:
+            ch.destroy()
+
+
+def _capture(ch, rank, xin, out, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for k in range(xin.shape[0]):
+            ch.allreduce(rank, xin[k], out[k], stream)
+    return g
+
+
+def _replay_both(graphs, streams):
+    torch.cuda.synchronize()
+    with torch.cuda.stream(streams[0]):
+        graphs[0].replay()
+    with torch.cuda.stream(streams[1]):
+        graphs[1].replay()
+    streams[0].synchronize()
+    streams[1].synchronize()
+
+
+def test_workload5_graph_of_1000_calls(channel, streams):
+    """Each rank captures 1000 calls into its own graph; both graphs are
+    captured and instantiated before either is launched, then both replay
+    concurrently; all 2000 outputs match the oracle."""
+    calls = 1000
+    xb = inputs.workload5(calls=calls)
+    say("exchange: workload 5, graph of 1000 calls N=10240")
+    xin = [to_dev(xb[r].reshape(-1)).view(calls, -1) for r in range(2)]
+    outs = [torch.empty_like(xin[r]) for r in range(2)]
+    # one eager call per rank before capture
+    loopback(channel, xin[0][0], xin[1][0], outs[0][0], outs[1][0], streams)
+    graphs = [_capture(channel, r, xin[r], outs[r], streams[r]) for r in range(2)]
+    outs[0].zero_()
+    outs[1].zero_()
+    _replay_both(graphs, streams)
+    assert channel.status() == hr.HR_OK
+    ref = oracle.add(xb[0].reshape(-1), xb[1].reshape(-1))
+    g0, g1 = to_host(outs[0]).reshape(-1), to_host(outs[1]).reshape(-1)
+    assert_same_bits(g0, ref, "graph rank 0")
+    assert_same_bits(g1, ref, "graph rank 1")
+    assert np.array_equal(g0, g1)
+
+
+def test_graph_replays_with_odd_call_count_and_fresh_inputs(channel, streams):
+    calls, n = 3, 10_240
+    xin = [torch.empty((calls, n), dtype=torch.float16, device="cuda:0") for _ in range(2)]
+    outs = [torch.empty_like(xin[r]) for r in range(2)]
+    loopback(channel, xin[0][0], xin[1][0], outs[0][0], outs[1][0], streams)
+    graphs = [_capture(channel, r, xin[r], outs[r], streams[r]) for r in range(2)]
+    for replay in range(4):
+        xb = [np.stack([inputs.gaussian(n, 1.0, 40 + replay, r, k) for k in range(calls)])
+              for r in range(2)]
+        for r in range(2):
+            xin[r].copy_(to_dev(xb[r].reshape(-1)).view(calls, n))
+        _replay_both(graphs, streams)
+        assert channel.status() == hr.HR_OK
+        ref = oracle.add(xb[0].reshape(-1), xb[1].reshape(-1))
+        assert_same_bits(to_host(outs[0]).reshape(-1), ref, f"replay {replay} rank 0")
+        assert_same_bits(to_host(outs[1]).reshape(-1), ref, f"replay {replay} rank 1")
+        # eager calls between replays keep the device-side parity consistent
+        x0b, x1b = inputs.workload2(1, call=replay)
+        x0, x1 = to_dev(x0b), to_dev(x1b)
+        o0, o1 = torch.empty_like(x0), torch.empty_like(x1)
+        loopback(channel, x0, x1, o0, o1, streams)
+        check_pair(o0, o1, x0b, x1b, f"eager after replay {replay}")
