@@ -1,0 +1,548 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP16 all-reduce combine on one MI355X.
+
+Headline (the JSON line's ``value``): the two-rank exchange through pinned
+host slots at 32 tokens x hidden 4096 = 131072 binary16 values (256 KiB) per
+rank, both ranks on one GPU (loopback), each rank's K calls captured into
+its own hipGraph and replayed together.  One step = one all-reduce call of
+both ranks.  ``value`` is algorithmic GB/s = (G + 1) * N * 2 bytes per call
+over the per-call time (G = 2); the roofline peak of this path is the
+host-link bandwidth measured in the same run by a pinned hipMemcpy probe.
+
+Also reported in the same line (``configs``): every workload's us/call,
+GB/s and fraction of its roofline -- the two-rank fold with planted specials
+in HBM, the exchange at 1..32 tokens eager and graph-captured, the eight-rank
+decode-sized and prefill-sized folds in HBM (cold and warm cache), and the
+graph of 1000 exchange calls with fresh inputs per call -- plus the host-link
+probe and the CPU oracle timed on this host's cores.
+
+Every timed output is checked bit for bit against the CPU oracle.
+
+Usage: python bench.py [--steps K] [--warmup W] [--quick] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and GB/s (% of HBM / host-link roofline), FP16 all-reduce combine"
+HBM_PEAK_GBS = 8000.0
+HIDDEN = 4096
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000, help="timed calls (one graph replay)")
+    p.add_argument("--warmup", type=int, default=200, help="untimed eager calls")
+    p.add_argument("--tokens", type=int, default=32)
+    p.add_argument("--quick", action="store_true", help="headline only")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    p.add_argument("--only", default="", help="comma list of sections: probe,exchange,fold,c5")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ helpers
+
+class Ctx:
+    def __init__(self):
+        import numpy as np
+        import torch
+        from message_fp16_all_amd import hr, inputs
+        self.np, self.torch, self.hr, self.inputs = np, torch, hr, inputs
+        self.dev = torch.device("cuda", 0)
+        self.streams = hr.LoopbackStreams(0)
+        self.gate_stream = torch.cuda.Stream()
+        self.sleep_rate = None  # sleep-kernel cycles per ms
+
+    def to_dev(self, bits):
+        np, torch = self.np, self.torch
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).to(self.dev)
+
+    def to_host(self, t):
+        np, torch = self.np, self.torch
+        return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def calibrate_sleep(self):
+        torch = self.torch
+        s = self.gate_stream
+        cycles = 2_000_000
+        for _ in range(2):
+            e0, e1 = self.event(), self.event()
+            with torch.cuda.stream(s):
+                e0.record(s)
+                torch.cuda._sleep(cycles)
+                e1.record(s)
+            s.synchronize()
+            ms = e0.elapsed_time(e1)
+        self.sleep_rate = cycles / max(ms, 1e-3)
+
+    def gate(self, ms):
+        """Event that completes `ms` milliseconds from now on the gate stream."""
+        torch = self.torch
+        if self.sleep_rate is None:
+            self.calibrate_sleep()
+        ev = torch.cuda.Event()
+        with torch.cuda.stream(self.gate_stream):
+            torch.cuda._sleep(int(self.sleep_rate * ms))
+            ev.record(self.gate_stream)
+        return ev
+
+
+def same(np_mod, got, ref):
+    import oracle
+    return bool(oracle.same_bits(got, ref).all())
+
+
+# ----------------------------------------------------------- host-link probe
+
+def host_link_probe(c: Ctx):
+    torch = c.torch
+    out = {}
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    for label, nbytes in (("20KiB", 20 * 1024), ("256KiB", 256 * 1024), ("64MiB", 64 << 20)):
+        h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        h2 = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        d = torch.empty(nbytes, dtype=torch.uint8, device=c.dev)
+        d2 = torch.empty(nbytes, dtype=torch.uint8, device=c.dev)
+        res = {}
+        for kind in ("h2d", "d2h", "bidir"):
+            times = []
+            for it in range(25):
+                e0, e1 = c.event(), c.event()
+                torch.cuda.synchronize()
+                e0.record(s0)
+                s1.wait_event(e0)
+                if kind in ("h2d", "bidir"):
+                    with torch.cuda.stream(s0):
+                        d.copy_(h, non_blocking=True)
+                if kind in ("d2h", "bidir"):
+                    with torch.cuda.stream(s1):
+                        h2.copy_(d2, non_blocking=True)
+                e_s1 = torch.cuda.Event()
+                e_s1.record(s1)
+                s0.wait_event(e_s1)
+                e1.record(s0)
+                torch.cuda.synchronize()
+                if it >= 5:
+                    times.append(e0.elapsed_time(e1) * 1e-3)
+            t = statistics.median(times)
+            moved = nbytes * (2 if kind == "bidir" else 1)
+            res[kind] = {"us": round(t * 1e6, 2), "GBps": round(moved / t / 1e9, 2)}
+        out[label] = res
+    peak = max(out["64MiB"]["h2d"]["GBps"], out["64MiB"]["d2h"]["GBps"])
+    return out, peak
+
+
+# ------------------------------------------------------------ the exchange
+
+def capture_calls(c: Ctx, ch, rank, xin, out, stream, calls):
+    torch = c.torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for k in range(calls):
+            xi = xin[k] if xin.dim() == 2 else xin
+            xo = out[k] if out.dim() == 2 else out
+            ch.allreduce(rank, xi, xo, stream)
+    return g
+
+
+def replay_pair(c: Ctx, graphs, gate_ms):
+    """Replay both ranks' graphs behind a common device-side gate; returns
+    (elapsed seconds on the GPU from gate open to both graphs done, host
+    submission seconds)."""
+    torch = c.torch
+    s0, s1 = c.streams
+    torch.cuda.synchronize()
+    gate = c.gate(gate_ms)
+    s0.wait_event(gate)
+    s1.wait_event(gate)
+    e0, e1, e_s1 = c.event(), c.event(), torch.cuda.Event()
+    e0.record(s0)
+    t_host = time.perf_counter()
+    with torch.cuda.stream(s0):
+        graphs[0].replay()
+    with torch.cuda.stream(s1):
+        graphs[1].replay()
+    t_host = time.perf_counter() - t_host
+    e_s1.record(s1)
+    s0.wait_event(e_s1)
+    e1.record(s0)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3, t_host
+
+
+def eager_pairs(c: Ctx, ch, x, o, calls):
+    torch = c.torch
+    s0, s1 = c.streams
+    torch.cuda.synchronize()
+    e0, e1, e_s1 = c.event(), c.event(), torch.cuda.Event()
+    e0.record(s0)
+    s1.wait_event(e0)
+    for _ in range(calls):
+        ch.allreduce(0, x[0], o[0], s0)
+        ch.allreduce(1, x[1], o[1], s1)
+    e_s1.record(s1)
+    s0.wait_event(e_s1)
+    e1.record(s0)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / calls
+
+
+def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls=200):
+    import oracle
+    torch, hr, inputs = c.torch, c.hr, c.inputs
+    x0b, x1b = inputs.workload2(tokens)
+    n = x0b.size
+    x = [c.to_dev(x0b), c.to_dev(x1b)]
+    o = [torch.empty_like(x[0]), torch.empty_like(x[1])]
+    ref = oracle.add(x0b, x1b)
+    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=5_000_000)
+    try:
+        for _ in range(warmup):
+            ch.allreduce(0, x[0], o[0], c.streams[0])
+            ch.allreduce(1, x[1], o[1], c.streams[1])
+        torch.cuda.synchronize()
+        t_eager = eager_pairs(c, ch, x, o, eager_calls)
+        graphs = [capture_calls(c, ch, r, x[r], o[r], c.streams[r], steps) for r in range(2)]
+        gate_ms = 5.0 + steps * 0.01
+        for _ in range(2):                       # upload + settle, untimed
+            replay_pair(c, graphs, gate_ms)
+        o[0].zero_()
+        o[1].zero_()
+        torch.cuda.synchronize()
+        elapsed, host_s = replay_pair(c, graphs, gate_ms)
+        if ch.status() != hr.HR_OK:
+            raise RuntimeError(f"exchange failed: {hr.hr_status_str(ch.status())}")
+        exact = same(c.np, c.to_host(o[0]), ref) and same(c.np, c.to_host(o[1]), ref)
+        del graphs
+        torch.cuda.synchronize()
+    finally:
+        ch.destroy()
+    t_graph = elapsed / steps
+    alg = 3 * n * 2
+    return {
+        "tokens": tokens, "N": n, "bytes_per_call": alg,
+        "graph_us": round(t_graph * 1e6, 3), "graph_GBps": round(alg / t_graph / 1e9, 2),
+        "graph_frac_link": round(alg / t_graph / 1e9 / link_peak, 4),
+        "link_GBps_per_dir": round(2 * n * 2 / t_graph / 1e9, 2),
+        "eager_us": round(t_eager * 1e6, 3), "eager_GBps": round(alg / t_eager / 1e9, 2),
+        "eager_frac_link": round(alg / t_eager / 1e9 / link_peak, 4),
+        "graph_calls": steps, "gate_ms": gate_ms, "host_submit_ms": round(host_s * 1e3, 3),
+        "gate_covered_submit": host_s * 1e3 < gate_ms,
+        "bit_exact": exact,
+        "_elapsed_s": elapsed,
+    }
+
+
+def workload5(c: Ctx, link_peak):
+    import oracle
+    torch, hr, inputs = c.torch, c.hr, c.inputs
+    calls = 1000
+    xb = inputs.workload5(calls=calls)
+    n = xb.shape[2]
+    xin = [c.to_dev(xb[r].reshape(-1)).view(calls, n) for r in range(2)]
+    outs = [torch.empty_like(xin[r]) for r in range(2)]
+    ch = hr.Channel(timeout_us=5_000_000)
+    try:
+        for k in range(4):
+            ch.allreduce(0, xin[0][k], outs[0][k], c.streams[0])
+            ch.allreduce(1, xin[1][k], outs[1][k], c.streams[1])
+        torch.cuda.synchronize()
+        graphs = [capture_calls(c, ch, r, xin[r], outs[r], c.streams[r], calls) for r in range(2)]
+        replay_pair(c, graphs, 15.0)
+        outs[0].zero_()
+        outs[1].zero_()
+        torch.cuda.synchronize()
+        elapsed, host_s = replay_pair(c, graphs, 15.0)
+        if ch.status() != hr.HR_OK:
+            raise RuntimeError(f"exchange failed: {hr.hr_status_str(ch.status())}")
+        ref = oracle.add(xb[0].reshape(-1), xb[1].reshape(-1))
+        exact = (same(c.np, c.to_host(outs[0]).reshape(-1), ref) and
+                 same(c.np, c.to_host(outs[1]).reshape(-1), ref))
+        del graphs
+        torch.cuda.synchronize()
+    finally:
+        ch.destroy()
+    t = elapsed / calls
+    alg = 3 * n * 2
+    return {"N": n, "calls": calls, "us_per_call": round(t * 1e6, 3),
+            "GBps": round(alg / t / 1e9, 2), "frac_link": round(alg / t / 1e9 / link_peak, 4),
+            "host_submit_ms": round(host_s * 1e3, 3), "bit_exact": exact}
+
+
+# ------------------------------------------------------------ the HBM fold
+
+def fold_time_warm(c: Ctx, ts, out, reps):
+    torch, hr = c.torch, c.hr
+    s = torch.cuda.current_stream()
+    hr.reduce(ts, out)
+    torch.cuda.synchronize()
+    e0, e1 = c.event(), c.event()
+    e0.record(s)
+    for _ in range(reps):
+        hr.reduce(ts, out)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def fold_time_graph(c: Ctx, ts, out, calls):
+    torch, hr = c.torch, c.hr
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(calls):
+            hr.reduce(ts, out, s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = c.event(), c.event()
+    cur = torch.cuda.current_stream()
+    e0.record(cur)
+    g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / calls
+
+
+def fold_time_cold(c: Ctx, ts, out, reps, flush):
+    torch, hr = c.torch, c.hr
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        flush.add_(1)                       # 512 MiB write evicts the 256 MB MALL
+        e0, e1 = c.event(), c.event()
+        e0.record(s)
+        hr.reduce(ts, out)
+        e1.record(s)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    return statistics.median(times)
+
+
+def fold_workload(c: Ctx, name, xs, cold=False, flush=None):
+    import oracle
+    torch = c.torch
+    G, n = len(xs), xs[0].size
+    ts = [c.to_dev(x) for x in xs]
+    out = torch.empty_like(ts[0])
+    alg = (G + 1) * n * 2
+    res = {"G": G, "N": n, "bytes_per_call": alg}
+    warm = fold_time_warm(c, ts, out, reps=200 if n < 1_000_000 else 50)
+    res["warm_us"] = round(warm * 1e6, 3)
+    res["warm_GBps"] = round(alg / warm / 1e9, 2)
+    res["warm_frac_hbm"] = round(alg / warm / 1e9 / HBM_PEAK_GBS, 4)
+    if n < 1_000_000:
+        gt = fold_time_graph(c, ts, out, calls=100)
+        res["graph_us"] = round(gt * 1e6, 3)
+        res["graph_GBps"] = round(alg / gt / 1e9, 2)
+        res["graph_frac_hbm"] = round(alg / gt / 1e9 / HBM_PEAK_GBS, 4)
+    if cold:
+        ct = fold_time_cold(c, ts, out, reps=30, flush=flush)
+        res["cold_us"] = round(ct * 1e6, 3)
+        res["cold_GBps"] = round(alg / ct / 1e9, 2)
+        res["cold_frac_hbm"] = round(alg / ct / 1e9 / HBM_PEAK_GBS, 4)
+    torch.cuda.synchronize()
+    ref = oracle.fold(xs, threads=8)[0] if n >= 1_000_000 else oracle.fold(xs)
+    res["bit_exact"] = same(c.np, c.to_host(out), ref)
+    del ts, out
+    return res
+
+
+# -------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(c: Ctx, tokens):
+    """The oracle, as it stands, on this host's cores: the headline's two
+    contributions folded repeatedly for a bounded time."""
+    import oracle
+    x0b, x1b = c.inputs.workload2(tokens)
+    n = x0b.size
+    alg = 3 * n * 2
+    cores = len(os.sched_getaffinity(0))
+    res = {}
+    # all cores, about 1.5 s wall
+    calls, t0 = 0, time.perf_counter()
+    used = 1
+    while True:
+        _, used = oracle.fold([x0b, x1b], threads=cores) if cores > 1 else (oracle.fold([x0b, x1b]), 1)
+        calls += 1
+        if time.perf_counter() - t0 > 1.5 and calls >= 3:
+            break
+    t = (time.perf_counter() - t0) / calls
+    res["all"] = {"us_per_call": t * 1e6, "GBps": alg / t / 1e9, "cores": used, "calls": calls}
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.fold([x0b, x1b])
+        calls += 1
+        if time.perf_counter() - t0 > 3.0 and calls >= 3:
+            break
+    t = (time.perf_counter() - t0) / calls
+    res["one"] = {"us_per_call": t * 1e6, "GBps": alg / t / 1e9, "cores": 1, "calls": calls}
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+# ---------------------------------------------------- counters (profiles/)
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("fold.hip", "exchange.hip", "hr_internal.h"):
+        with open(os.path.join(ROOT, "message_fp16_all_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM/host bytes per launch of `kernel` from the committed counter
+    summary, or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "counters.txt")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest()
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"traffic\s+(\S+)\s+(\S+)\s+sources=(\S+)", line.strip())
+            if m and m.group(1) == kernel and m.group(3) == digest:
+                return float(m.group(2))
+    return None
+
+
+# -------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    c = Ctx()
+    torch = c.torch
+    only = set(filter(None, args.only.split(",")))
+    want = (lambda s: not only or s in only)
+    props = torch.cuda.get_device_properties(0)
+    cfgs = {}
+
+    log("host-link probe")
+    probe, link_peak = host_link_probe(c)
+    cfgs["host_link_probe"] = probe
+
+    log(f"headline: exchange graph, tokens={args.tokens}, K={args.steps}")
+    head = exchange_workload(c, args.tokens, args.steps, args.warmup, link_peak)
+    elapsed = head.pop("_elapsed_s")
+
+    if not args.quick:
+        if want("exchange"):
+            rows = []
+            for t in c.inputs.TOKENS_EXCHANGE:
+                log(f"exchange tokens={t}")
+                r = exchange_workload(c, t, 500, 50, link_peak)
+                r.pop("_elapsed_s")
+                rows.append(r)
+            cfgs["exchange_2rank_host_slots"] = rows
+        if want("c5"):
+            log("exchange graph of 1000 fresh calls, N=10240")
+            cfgs["exchange_graph_1000_calls_N10240"] = workload5(c, link_peak)
+        if want("fold"):
+            log("fold G=2 N=4096 with specials")
+            cfgs["fold_G2_N4096_specials"] = fold_workload(c, "w1", c.inputs.workload1()[0])
+            log("fold G=8 N=393216")
+            cfgs["fold_G8_N393216"] = fold_workload(c, "w3", c.inputs.workload3())
+            log("fold G=8 N=16777216")
+            flush = torch.zeros(512 << 20, dtype=torch.uint8, device=c.dev)
+            cfgs["fold_G8_N16777216"] = fold_workload(c, "w4", c.inputs.workload4(), cold=True,
+                                                      flush=flush)
+            del flush
+
+    cpu = None
+    if not args.no_cpu:
+        log("CPU oracle baseline")
+        cpu = cpu_baseline(c, args.tokens)
+
+    c.streams.destroy()
+    t_call = elapsed / args.steps
+    n = head["N"]
+    alg = 3 * n * 2
+    achieved = alg / t_call / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(achieved, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_call * 1e3, 6),
+        "us_per_call": round(t_call * 1e6, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: seeded N(0, 0.5^2) binary16 per rank",
+        "config": {"workload": "two-rank FP16 all-reduce through pinned host slots, loopback on "
+                               "one GPU, graph-captured",
+                   "G": 2, "tokens": args.tokens, "hidden": HIDDEN, "N": n,
+                   "bytes_per_call": alg, "calls_per_graph": args.steps,
+                   "parallelism": "none (one GPU; two ranks as two co-resident launches)"},
+        "roofline": {"bound": "host-link", "achieved": round(achieved, 3), "peak": link_peak,
+                     "unit": "GB/s", "frac": round(achieved / link_peak, 4),
+                     "traffic": measured_traffic("exchange_f16"),
+                     "kernel": "hr::exchange_f16<u32x4>",
+                     "peak_source": "pinned hipMemcpyAsync probe, max(H2D, D2H) at 64 MiB, this run",
+                     "link_GBps_per_dir": head["link_GBps_per_dir"]},
+        "bit_exact": head["bit_exact"],
+        "headline": head,
+        "configs": cfgs,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "hip": torch.version.hip, "torch": torch.__version__},
+        "host": {"cpu": cpu_model(), "cores": len(os.sched_getaffinity(0))},
+    }
+    if "fold_G8_N16777216" in cfgs:
+        f4 = cfgs["fold_G8_N16777216"]
+        line["roofline_hbm_fold"] = {
+            "bound": "hbm", "kernel": "hr::fold_f16_vec<8,2>", "G": 8, "N": f4["N"],
+            "achieved": f4["cold_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": f4["cold_frac_hbm"], "warm_frac": f4["warm_frac_hbm"],
+            "traffic": measured_traffic("fold_f16_vec<8,2>"),
+        }
+    if cpu is not None:
+        line["cpu_baseline"] = {
+            "value": round(cpu["all"]["GBps"], 4), "unit": "GB/s", "cores": cpu["all"]["cores"],
+            "kind": "oracle",
+            "sample": f"the headline's two {n}-value contributions folded by the C oracle "
+                      f"{cpu['all']['calls']} times (~1.5 s wall) on all cores",
+            "us_per_call": round(cpu["all"]["us_per_call"], 2),
+            "one_core": {"us_per_call": round(cpu["one"]["us_per_call"], 2),
+                         "GBps": round(cpu["one"]["GBps"], 4), "calls": cpu["one"]["calls"]},
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

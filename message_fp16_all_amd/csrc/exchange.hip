@@ -21,16 +21,18 @@
 //     device error word.
 //
 // Call protocol of workgroup b of rank r at call e (= its counter + 1):
-//   1. load its slice of `in` and store it to slot[e & 1][r]        (D2H)
-//   2. every lane: system-scope fence; barrier; lane 0: release-store
-//      flag[r][b] = e at system scope
-//   3. lane 0 polls flag[peer][b] with system-scope acquire loads until it
-//      reaches e (wrap-safe signed compare, so a peer already at e + 1 also
+//   1. load its slice of `in` and store it to slot[e & 1][r] with
+//      system-coherent (write-through) stores                        (D2H)
+//   2. every lane waits for its stores to be acknowledged; barrier; lane 0
+//      stores flag[r][b] = e at system scope -- the "fence, then flag" of
+//      the method, without a whole-cache write-back
+//   3. lane 0 polls flag[peer][b] with system-scope loads until it reaches
+//      e (wrap-safe signed compare, so a peer already at e + 1 also
 //      releases the wait), sleeping between polls; it also polls the abort
 //      word and a watchdog on the constant-rate wall clock
-//   4. barrier, acquire fence, load slot[e & 1][peer] (H2D) and its own
-//      slice of `in` again, store fl16(x0 + x1) with rank 0's value first
-//      to `out`.
+//   4. barrier, then system-coherent loads of slot[e & 1][peer] (H2D) and
+//      plain loads of its own slice of `in` again; store fl16(x0 + x1)
+//      with rank 0's value first to `out`.
 // Why one parity cannot be overwritten while the peer still reads it: a
 // rank's workgroup publishes call e + 2 (same parity as e) only after its
 // wait in call e + 1 saw the peer's flag of call e + 1, which the peer raises
@@ -73,6 +75,43 @@ struct ExchArgs {
 __device__ __forceinline__ u32x4 combine(u32x4 x0, u32x4 x1) { return add_f16x8(x0, x1); }
 __device__ __forceinline__ uint16_t combine(uint16_t x0, uint16_t x1) { return add_f16x1(x0, x1); }
 
+// Host-slot accesses are buffer loads/stores with the system-coherence bits
+// (sc0 sc1): stores write through every GPU cache level to host memory and
+// loads fetch from it, so the exchange needs no cache write-back or
+// invalidate (which a system-scope fence would do for the whole L2).  The
+// descriptor's third dword selects 32-bit data format for raw (untyped)
+// access; num_records bounds every access to the slot.
+constexpr int kSysCoherent = 1 | 16;                  // sc0 | sc1
+constexpr int kRawBufferDword3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const uint16_t *base, size_t values) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0,
+                                             static_cast<int>(values * sizeof(uint16_t)), kRawBufferDword3);
+}
+
+template <typename T>
+struct HostIO;
+
+template <>
+struct HostIO<u32x4> {
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, size_t unit, u32x4 v) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(unit * 16), 0, kSysCoherent);
+    }
+    static __device__ __forceinline__ u32x4 load(__amdgpu_buffer_rsrc_t r, size_t unit) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(unit * 16), 0, kSysCoherent);
+    }
+};
+
+template <>
+struct HostIO<uint16_t> {
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, size_t unit, uint16_t v) {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, static_cast<int>(unit * 2), 0, kSysCoherent);
+    }
+    static __device__ __forceinline__ uint16_t load(__amdgpu_buffer_rsrc_t r, size_t unit) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(unit * 2), 0, kSysCoherent);
+    }
+};
+
 // T is the unit of one lane access: u32x4 (8 values, 16-byte aligned
 // buffers) or uint16_t (1 value, any 2-byte aligned buffers).
 template <typename T>
@@ -104,10 +143,12 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
 
     const T *in = static_cast<const T *>(a.in);
     T *out = static_cast<T *>(a.out);
-    T *mine = reinterpret_cast<T *>(a.slots + (static_cast<size_t>(2 * parity + a.rank)) * a.stride);
-    const T *theirs = reinterpret_cast<const T *>(a.slots + (static_cast<size_t>(2 * parity + peer)) * a.stride);
+    const __amdgpu_buffer_rsrc_t mine =
+        slot_rsrc(a.slots + static_cast<size_t>(2 * parity + a.rank) * a.stride, a.stride);
+    const __amdgpu_buffer_rsrc_t theirs =
+        slot_rsrc(a.slots + static_cast<size_t>(2 * parity + peer) * a.stride, a.stride);
 
-    // 1. publish this rank's slice into its host slot
+    // 1. publish this rank's slice into its host slot (write-through)
     for (size_t v0 = lo + tid; v0 < hi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
         T x[kExchUnroll];
 #pragma unroll
@@ -118,28 +159,26 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
 #pragma unroll
         for (int u = 0; u < kExchUnroll; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < hi) mine[v] = x[u];
+            if (v < hi) HostIO<T>::store(mine, v, x[u]);
         }
     }
-    if (last && tail0 + tid < a.numel) {
-        const uint16_t *in16 = static_cast<const uint16_t *>(a.in);
-        uint16_t *mine16 = a.slots + (static_cast<size_t>(2 * parity + a.rank)) * a.stride;
-        mine16[tail0 + tid] = in16[tail0 + tid];
-    }
+    if (last && tail0 + tid < a.numel)
+        HostIO<uint16_t>::store(mine, tail0 + tid, static_cast<const uint16_t *>(a.in)[tail0 + tid]);
 
-    // 2. every lane's slot stores are visible system-wide before the flag
-    __threadfence_system();
+    // 2. every lane waits until its slot stores are acknowledged, so they
+    //    are in host memory before lane 0 raises the flag
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // 3. raise this workgroup's flag, then wait for the peer's
     if (tid == 0) {
         __hip_atomic_store(a.flags + (static_cast<size_t>(a.rank) * a.nblocks + b) * kFlagStride, e,
-                           __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         const uint32_t *pf = a.flags + (static_cast<size_t>(peer) * a.nblocks + b) * kFlagStride;
         uint32_t status = 0;
         const long long t0 = wall_clock64();
         for (;;) {
-            const uint32_t f = __hip_atomic_load(pf, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
+            const uint32_t f = __hip_atomic_load(pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             if (static_cast<int32_t>(f - e) >= 0) break;
             if (__hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) {
                 status = HR_ERR_ABORTED;
@@ -153,14 +192,14 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
         }
         if (status != 0) {
             __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.host_error, status, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(a.host_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
         s_status = status;
     }
+    // the barrier orders every lane's slot loads after the flag lane 0 saw;
+    // the loads themselves read host memory, not a cached copy
     __syncthreads();
     if (s_status != 0) return;
-    // order every lane's slot loads after the flag observed by lane 0
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 
     // 4. combine in rank order: x0 + x1
     for (size_t v0 = lo + tid; v0 < hi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
@@ -169,7 +208,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
         for (int u = 0; u < kExchUnroll; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
             if (v < hi) {
-                y[u] = theirs[v];
+                y[u] = HostIO<T>::load(theirs, v);
                 x[u] = in[v];
             }
         }
@@ -180,9 +219,8 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
         }
     }
     if (last && tail0 + tid < a.numel) {
-        const uint16_t *in16 = static_cast<const uint16_t *>(a.in);
-        const uint16_t *theirs16 = a.slots + (static_cast<size_t>(2 * parity + peer)) * a.stride;
-        const uint16_t xv = in16[tail0 + tid], yv = theirs16[tail0 + tid];
+        const uint16_t xv = static_cast<const uint16_t *>(a.in)[tail0 + tid];
+        const uint16_t yv = HostIO<uint16_t>::load(theirs, tail0 + tid);
         static_cast<uint16_t *>(a.out)[tail0 + tid] = (a.rank == 0) ? add_f16x1(xv, yv) : add_f16x1(yv, xv);
     }
 }
