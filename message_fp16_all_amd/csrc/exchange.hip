@@ -20,7 +20,13 @@
 //   device (HBM): epoch[2 rank][nblocks] -- per-workgroup call counter,
 //     device error word.
 //
-// Call protocol of workgroup b of rank r at call e (= its counter + 1):
+// Every launch has the channel's fixed workgroup count; each workgroup
+// advances its call counter, so parity is uniform across a call.  Only the
+// first `nactive` workgroups (a function of numel, so equal on both ranks)
+// carry values and take part in the flag handshake: fewer pollers means less
+// non-posted traffic on the host link, which is what bounds small calls.
+//
+// Call protocol of active workgroup b of rank r at call e (= its counter + 1):
 //   1. load its slice of `in` and store it to slot[e & 1][r] with
 //      system-coherent (write-through) stores                        (D2H)
 //   2. every lane waits for its stores to be acknowledged; barrier; lane 0
@@ -34,9 +40,10 @@
 //      plain loads of its own slice of `in` again; store fl16(x0 + x1)
 //      with rank 0's value first to `out`.
 // Why one parity cannot be overwritten while the peer still reads it: a
-// rank's workgroup publishes call e + 2 (same parity as e) only after its
-// wait in call e + 1 saw the peer's flag of call e + 1, which the peer raises
-// only after its whole call-e kernel has finished (stream order).
+// rank starts call e + 2 (same parity as e) only after its call e + 1 has
+// finished, and in call e + 1 its workgroup 0 (always active) waited for the
+// peer's flag of call e + 1, which the peer raises only after its whole
+// call-e kernel has finished (stream order).
 //
 // Errors (timeout, abort) are written to the device error word and the
 // host-mapped error word; a kernel that finds the device word set returns at
@@ -47,12 +54,14 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 namespace hr {
 
 constexpr int kExchThreads = 256;
 constexpr int kExchUnroll = 4;
+constexpr int kMinActive = 8;
 constexpr size_t kLine = 128;                     // bytes per flag / word line
 constexpr size_t kFlagStride = kLine / sizeof(uint32_t);
 
@@ -69,7 +78,8 @@ struct ExchArgs {
     const uint32_t *abort_w;  // device view of the host abort word
     uint64_t timeout_ticks;
     int rank;
-    int nblocks;
+    int nblocks;   // launched workgroups (the channel's fixed count)
+    int nactive;   // workgroups that carry values in this call
 };
 
 __device__ __forceinline__ u32x4 combine(u32x4 x0, u32x4 x1) { return add_f16x8(x0, x1); }
@@ -112,15 +122,23 @@ struct HostIO<uint16_t> {
     }
 };
 
-// T is the unit of one lane access: u32x4 (8 values, 16-byte aligned
-// buffers) or uint16_t (1 value, any 2-byte aligned buffers).
-template <typename T>
+// Workgroup b of an active set of `nact` owns the 8-value units
+// [nvec*b/nact, nvec*(b+1)/nact) of the call, nvec = numel / 8, and the last
+// active workgroup also owns the numel % 8 trailing values.  The split
+// depends on numel alone, so workgroup b covers the same values on both
+// ranks whichever access path (16-byte or 2-byte) each rank takes.
+//
+// VEC selects the lane access unit: one 16-byte unit (all buffers 16-byte
+// aligned) or one value (2-byte aligned buffers).
+template <bool VEC>
 __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
     __shared__ uint32_t s_epoch;
     __shared__ uint32_t s_status;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
 
+    // Every launched workgroup advances its call counter, active or not, so
+    // all workgroups of a rank agree on the call's slot parity.
     if (tid == 0) {
         const uint32_t err = __hip_atomic_load(a.dev_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t e = __hip_atomic_load(&a.epochs[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
@@ -129,18 +147,20 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
         s_status = err;
     }
     __syncthreads();
-    if (s_status != 0) return;
+    if (s_status != 0 || b >= a.nactive) return;
     const uint32_t e = s_epoch;
     const int parity = static_cast<int>(e & 1u);
     const int peer = a.rank ^ 1;
 
-    constexpr size_t per = sizeof(T) / sizeof(uint16_t);
-    const size_t nunits = a.numel / per;
-    const size_t lo = nunits * static_cast<size_t>(b) / static_cast<size_t>(a.nblocks);
-    const size_t hi = nunits * static_cast<size_t>(b + 1) / static_cast<size_t>(a.nblocks);
-    const bool last = (b == a.nblocks - 1);
-    const size_t tail0 = nunits * per;  // first value not covered by whole units
+    const size_t nvec = a.numel / kVecElems;
+    const size_t lo = nvec * static_cast<size_t>(b) / static_cast<size_t>(a.nactive);
+    const size_t hi = nvec * static_cast<size_t>(b + 1) / static_cast<size_t>(a.nactive);
+    const bool last = (b == a.nactive - 1);
+    const size_t tail0 = nvec * kVecElems;  // first value not covered by whole units
 
+    typedef typename std::conditional<VEC, u32x4, uint16_t>::type T;
+    constexpr size_t per = VEC ? kVecElems : 1;  // values per lane access
+    const size_t ulo = lo * (kVecElems / per), uhi = hi * (kVecElems / per);
     const T *in = static_cast<const T *>(a.in);
     T *out = static_cast<T *>(a.out);
     const __amdgpu_buffer_rsrc_t mine =
@@ -149,17 +169,17 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
         slot_rsrc(a.slots + static_cast<size_t>(2 * parity + peer) * a.stride, a.stride);
 
     // 1. publish this rank's slice into its host slot (write-through)
-    for (size_t v0 = lo + tid; v0 < hi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
+    for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
         T x[kExchUnroll];
 #pragma unroll
         for (int u = 0; u < kExchUnroll; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < hi) x[u] = in[v];
+            if (v < uhi) x[u] = in[v];
         }
 #pragma unroll
         for (int u = 0; u < kExchUnroll; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < hi) HostIO<T>::store(mine, v, x[u]);
+            if (v < uhi) HostIO<T>::store(mine, v, x[u]);
         }
     }
     if (last && tail0 + tid < a.numel)
@@ -202,12 +222,12 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
     if (s_status != 0) return;
 
     // 4. combine in rank order: x0 + x1
-    for (size_t v0 = lo + tid; v0 < hi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
+    for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
         T y[kExchUnroll], x[kExchUnroll];
 #pragma unroll
         for (int u = 0; u < kExchUnroll; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < hi) {
+            if (v < uhi) {
                 y[u] = HostIO<T>::load(theirs, v);
                 x[u] = in[v];
             }
@@ -215,7 +235,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
 #pragma unroll
         for (int u = 0; u < kExchUnroll; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < hi) out[v] = (a.rank == 0) ? combine(x[u], y[u]) : combine(y[u], x[u]);
+            if (v < uhi) out[v] = (a.rank == 0) ? combine(x[u], y[u]) : combine(y[u], x[u]);
         }
     }
     if (last && tail0 + tid < a.numel) {
@@ -223,6 +243,18 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
         const uint16_t yv = HostIO<uint16_t>::load(theirs, tail0 + tid);
         static_cast<uint16_t *>(a.out)[tail0 + tid] = (a.rank == 0) ? add_f16x1(xv, yv) : add_f16x1(yv, xv);
     }
+}
+
+// Active workgroups for a call of numel values: about one 16-byte unit per
+// lane, at least kMinActive (so small calls still spread their flag traffic
+// over a few workgroups), at most the channel's workgroup count.  A function
+// of numel alone, so both ranks agree.
+inline int active_blocks(size_t numel, int nblocks) {
+    const size_t nvec = numel / kVecElems;
+    size_t want = (nvec + kExchThreads - 1) / kExchThreads;
+    if (want < static_cast<size_t>(kMinActive)) want = kMinActive;
+    if (want > static_cast<size_t>(nblocks)) want = static_cast<size_t>(nblocks);
+    return static_cast<int>(want);
 }
 
 }  // namespace hr
@@ -355,12 +387,13 @@ extern "C" HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void
     a.timeout_ticks = ch->timeout_ticks;
     a.rank = rank;
     a.nblocks = ch->nblocks;
+    a.nactive = active_blocks(numel, ch->nblocks);
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (aligned(in, 16) && aligned(out, 16))
-        hipLaunchKernelGGL(exchange_f16<u32x4>, dim3(ch->nblocks), dim3(kExchThreads), 0, s, a);
+        hipLaunchKernelGGL(exchange_f16<true>, dim3(ch->nblocks), dim3(kExchThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(exchange_f16<uint16_t>, dim3(ch->nblocks), dim3(kExchThreads), 0, s, a);
+        hipLaunchKernelGGL(exchange_f16<false>, dim3(ch->nblocks), dim3(kExchThreads), 0, s, a);
     return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
 }
 
