@@ -54,6 +54,13 @@ def parse():
     p.add_argument("--quick", action="store_true", help="headline only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--only", default="", help="comma list of sections: probe,exchange,fold,c5")
+    p.add_argument("--profile-kernel", choices=("fold", "exchange", "copy"), default=None,
+                   help="run one kernel --reps times and nothing else (for rocprofv3 counters)")
+    p.add_argument("--reps", type=int, default=10)
+    p.add_argument("--gate-ms", type=float, default=None,
+                   help="hold both rank streams this long before a timed replay (default "
+                        "5 ms + 10 us per call; raise it under a profiler, which slows graph "
+                        "submission)")
     return p.parse_args()
 
 
@@ -207,7 +214,7 @@ def eager_pairs(c: Ctx, ch, x, o, calls):
     return e0.elapsed_time(e1) * 1e-3 / calls
 
 
-def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls=200):
+def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls=200, gate_ms=None):
     import oracle
     torch, hr, inputs = c.torch, c.hr, c.inputs
     x0b, x1b = inputs.workload2(tokens)
@@ -223,7 +230,8 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls=200)
         torch.cuda.synchronize()
         t_eager = eager_pairs(c, ch, x, o, eager_calls)
         graphs = [capture_calls(c, ch, r, x[r], o[r], c.streams[r], steps) for r in range(2)]
-        gate_ms = 5.0 + steps * 0.01
+        if gate_ms is None:
+            gate_ms = 5.0 + steps * 0.01
         for _ in range(2):                       # upload + settle, untimed
             replay_pair(c, graphs, gate_ms)
         o[0].zero_()
@@ -323,12 +331,14 @@ def fold_time_graph(c: Ctx, ts, out, calls):
     return e0.elapsed_time(e1) * 1e-3 / calls
 
 
-def fold_time_cold(c: Ctx, ts, out, reps, flush):
+def fold_time_cold_single(c: Ctx, ts, out, reps, flush):
+    """One launch after a read-only pass over 512 MiB has replaced the MALL's
+    contents with clean lines; includes the single launch's dispatch."""
     torch, hr = c.torch, c.hr
     s = torch.cuda.current_stream()
     times = []
     for _ in range(reps):
-        flush.add_(1)                       # 512 MiB write evicts the 256 MB MALL
+        flush.sum()                          # reads 512 MiB, writes nothing back
         e0, e1 = c.event(), c.event()
         e0.record(s)
         hr.reduce(ts, out)
@@ -338,31 +348,71 @@ def fold_time_cold(c: Ctx, ts, out, reps, flush):
     return statistics.median(times)
 
 
-def fold_workload(c: Ctx, name, xs, cold=False, flush=None):
+def fold_time_rotating(c: Ctx, sets, outs, reps=30):
+    """Back-to-back launches cycling over >= 3 input sets (768 MiB for the
+    prefill-sized workload), so each launch finds none of its inputs in the
+    256 MB MALL; the per-launch time includes the dispatch gap."""
+    torch, hr = c.torch, c.hr
+    s = torch.cuda.current_stream()
+    k = len(sets)
+    for i in range(k):
+        hr.reduce(sets[i], outs[i])
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(3):
+        e0, e1 = c.event(), c.event()
+        e0.record(s)
+        for i in range(reps):
+            hr.reduce(sets[i % k], outs[i % k])
+        e1.record(s)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    return statistics.median(res)
+
+
+def fold_workload(c: Ctx, name, xs, prefill=False):
     import oracle
     torch = c.torch
     G, n = len(xs), xs[0].size
     ts = [c.to_dev(x) for x in xs]
     out = torch.empty_like(ts[0])
     alg = (G + 1) * n * 2
+
+    def rate(prefix, t, res):
+        res[prefix + "_us"] = round(t * 1e6, 3)
+        res[prefix + "_GBps"] = round(alg / t / 1e9, 2)
+        res[prefix + "_frac_hbm"] = round(alg / t / 1e9 / HBM_PEAK_GBS, 4)
+
     res = {"G": G, "N": n, "bytes_per_call": alg}
-    warm = fold_time_warm(c, ts, out, reps=200 if n < 1_000_000 else 50)
-    res["warm_us"] = round(warm * 1e6, 3)
-    res["warm_GBps"] = round(alg / warm / 1e9, 2)
-    res["warm_frac_hbm"] = round(alg / warm / 1e9 / HBM_PEAK_GBS, 4)
+    rate("warm", fold_time_warm(c, ts, out, reps=200 if n < 1_000_000 else 50), res)
     if n < 1_000_000:
-        gt = fold_time_graph(c, ts, out, calls=100)
-        res["graph_us"] = round(gt * 1e6, 3)
-        res["graph_GBps"] = round(alg / gt / 1e9, 2)
-        res["graph_frac_hbm"] = round(alg / gt / 1e9 / HBM_PEAK_GBS, 4)
-    if cold:
-        ct = fold_time_cold(c, ts, out, reps=30, flush=flush)
-        res["cold_us"] = round(ct * 1e6, 3)
-        res["cold_GBps"] = round(alg / ct / 1e9, 2)
-        res["cold_frac_hbm"] = round(alg / ct / 1e9 / HBM_PEAK_GBS, 4)
-    torch.cuda.synchronize()
+        rate("graph", fold_time_graph(c, ts, out, calls=100), res)
     ref = oracle.fold(xs, threads=8)[0] if n >= 1_000_000 else oracle.fold(xs)
-    res["bit_exact"] = same(c.np, c.to_host(out), ref)
+    exact = same(c.np, c.to_host(out), ref)
+    if prefill:
+        flush = torch.ones(512 << 20, dtype=torch.uint8, device=c.dev)
+        rate("cold_single", fold_time_cold_single(c, ts, out, 15, flush), res)
+        del flush
+        # three sets of separately allocated contributions (the caller's layout)
+        sets = [ts] + [[t.clone() for t in ts] for _ in range(2)]
+        outs = [out] + [torch.empty_like(out) for _ in range(2)]
+        rate("cold", fold_time_rotating(c, sets, outs), res)
+        exact = exact and all(same(c.np, c.to_host(o), ref) for o in outs)
+        del sets, outs
+        # the same with contributions 4 KiB apart inside one buffer per set,
+        # the layout a workspace owner can choose
+        stride = n + 2048
+        bufs = [torch.empty(G * stride, dtype=torch.float16, device=c.dev) for _ in range(3)]
+        sets = [[b[g * stride:g * stride + n] for g in range(G)] for b in bufs]
+        for st in sets:
+            for g in range(G):
+                st[g].copy_(ts[g])
+        outs = [torch.empty_like(out) for _ in range(3)]
+        rate("cold_staggered", fold_time_rotating(c, sets, outs), res)
+        exact = exact and all(same(c.np, c.to_host(o), ref) for o in outs)
+        del bufs, sets, outs
+    torch.cuda.synchronize()
+    res["bit_exact"] = exact
     del ts, out
     return res
 
@@ -435,6 +485,74 @@ def measured_traffic(kernel):
     return None
 
 
+# ------------------------------------------------------- profiling targets
+
+def profile_kernel(which, reps):
+    """Launch one kernel `reps` times with nothing else timed, for
+    rocprofv3 (counter collection serialises dispatches, so the exchange runs
+    one rank against a peer that the host plays: the host writes the peer's
+    slot and raises its flags before each launch)."""
+    import ctypes
+    import numpy as np
+    import torch
+    import oracle
+    from message_fp16_all_amd import hr, inputs
+    dev = torch.device("cuda", 0)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).to(dev)
+
+    if which == "copy":
+        # plain device copy of known size: 256 MiB read + 256 MiB written
+        src = torch.ones(128 << 20, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy: {reps} x 256 MiB")
+        return
+    if which == "fold":
+        xs = inputs.workload4()
+        ts = [to_dev(x) for x in xs]
+        out = torch.empty_like(ts[0])
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            hr.reduce(ts, out)
+        torch.cuda.synchronize()
+        ok = bool(oracle.same_bits(out.view(torch.int16).cpu().numpy().view(np.uint16),
+                                   oracle.fold(xs, threads=8)[0]).all())
+        log(f"fold G=8 N={xs[0].size}: {reps} launches, bit_exact={ok}")
+        return
+    x0b, x1b = inputs.workload2(32)
+    n = x0b.size
+    x0 = to_dev(x0b)
+    out = torch.empty_like(x0)
+    streams = hr.LoopbackStreams(0)
+    ch = hr.Channel(timeout_us=2_000_000)
+    info = ch.info()
+    ref = oracle.add(x0b, x1b)
+    ok = True
+    try:
+        for call in range(1, reps + 1):
+            parity = call & 1
+            peer_slot = info.host_slots + (2 * parity + 1) * info.slot_stride * 2
+            ctypes.memmove(peer_slot, x1b.ctypes.data, n * 2)
+            for b in range(info.num_blocks):
+                info.host_flags[(1 * info.num_blocks + b) * info.flag_stride] = call
+            torch.cuda.synchronize()
+            ch.allreduce(0, x0, out, streams[0])
+            streams[0].synchronize()
+            if ch.status() != hr.HR_OK:
+                raise RuntimeError(hr.hr_status_str(ch.status()))
+            got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+            ok = ok and bool(oracle.same_bits(got, ref).all())
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+        streams.destroy()
+    log(f"exchange rank 0 against a host-played peer, N={n}: {reps} calls, bit_exact={ok}")
+
+
 # -------------------------------------------------------------------- main
 
 def main():
@@ -443,6 +561,9 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.profile_kernel:
+        profile_kernel(args.profile_kernel, args.reps)
+        return
     c = Ctx()
     torch = c.torch
     only = set(filter(None, args.only.split(",")))
@@ -455,7 +576,8 @@ def main():
     cfgs["host_link_probe"] = probe
 
     log(f"headline: exchange graph, tokens={args.tokens}, K={args.steps}")
-    head = exchange_workload(c, args.tokens, args.steps, args.warmup, link_peak)
+    head = exchange_workload(c, args.tokens, args.steps, args.warmup, link_peak,
+                             gate_ms=args.gate_ms)
     elapsed = head.pop("_elapsed_s")
 
     if not args.quick:
@@ -476,10 +598,7 @@ def main():
             log("fold G=8 N=393216")
             cfgs["fold_G8_N393216"] = fold_workload(c, "w3", c.inputs.workload3())
             log("fold G=8 N=16777216")
-            flush = torch.zeros(512 << 20, dtype=torch.uint8, device=c.dev)
-            cfgs["fold_G8_N16777216"] = fold_workload(c, "w4", c.inputs.workload4(), cold=True,
-                                                      flush=flush)
-            del flush
+            cfgs["fold_G8_N16777216"] = fold_workload(c, "w4", c.inputs.workload4(), prefill=True)
 
     cpu = None
     if not args.no_cpu:
@@ -528,7 +647,9 @@ def main():
         line["roofline_hbm_fold"] = {
             "bound": "hbm", "kernel": "hr::fold_f16_vec<8,2>", "G": 8, "N": f4["N"],
             "achieved": f4["cold_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": f4["cold_frac_hbm"], "warm_frac": f4["warm_frac_hbm"],
+            "frac": f4["cold_frac_hbm"], "protocol": "3 rotating input sets, back-to-back",
+            "staggered_frac": f4["cold_staggered_frac_hbm"], "warm_frac": f4["warm_frac_hbm"],
+            "single_launch_frac": f4["cold_single_frac_hbm"],
             "traffic": measured_traffic("fold_f16_vec<8,2>"),
         }
     if cpu is not None:

@@ -12,9 +12,10 @@
 // at most 7/18 add per byte -- bound by HBM bandwidth, not by VALU; there is
 // no contraction, so no MFMA.
 //
-// Kernel shape.  Each lane owns U 16-byte units (8 values each) per tile and
-// issues all G*U dwordx4 loads before the first add, so every lane keeps
-// G*U*16 bytes in flight; the adds run in rank order as packed
+// Kernel shape.  Workgroups of 128 lanes; each lane owns U 16-byte units (8
+// values each) per tile and issues all G*U dwordx4 loads before the first
+// add, so every lane keeps G*U*16 bytes in flight; the adds run in rank
+// order as packed
 // v_pk_add_f16; U dwordx4 stores follow.  Loads and stores are non-temporal:
 // every byte is touched once, so caching it would only evict useful lines.
 // A grid-stride loop over tiles covers any N; the N % 8 tail is folded one
@@ -26,7 +27,7 @@
 
 namespace hr {
 
-constexpr int kFoldThreads = 256;
+constexpr int kFoldThreads = 128;
 
 struct FoldArgs {
     const void *in[HR_MAX_G];
@@ -102,9 +103,9 @@ template <int G>
 hipError_t launch_vec(const FoldArgs &a, int cus, hipStream_t s) {
     constexpr int U = FoldShape<G>::U;
     const size_t tiles = (a.nvec + static_cast<size_t>(kFoldThreads) * U - 1) / (static_cast<size_t>(kFoldThreads) * U);
-    // Enough workgroups to fill every CU several times over; beyond that the
+    // Enough workgroups to fill every CU many times over; beyond that the
     // grid-stride loop takes over so huge N does not mean huge grids.
-    const size_t cap = static_cast<size_t>(cus) * 16;
+    const size_t cap = static_cast<size_t>(cus) * 32;
     size_t grid = tiles < cap ? tiles : cap;
     if (grid == 0) grid = 1;  // the tail alone
     hipLaunchKernelGGL((fold_f16_vec<G, U>), dim3(static_cast<unsigned>(grid)), dim3(kFoldThreads), 0, s, a);
@@ -191,7 +192,7 @@ extern "C" HR_API hr_status hr_reduce_f16(const void *const *inputs, int G, void
         e = launch_vec_g(G, a, cus, s);
     } else {
         const size_t blocks = (numel + kFoldThreads - 1) / kFoldThreads;
-        const size_t cap = static_cast<size_t>(cus) * 16;
+        const size_t cap = static_cast<size_t>(cus) * 32;
         hipLaunchKernelGGL(fold_f16_scalar, dim3(static_cast<unsigned>(blocks < cap ? blocks : cap)),
                            dim3(kFoldThreads), 0, s, a, G);
         e = hipGetLastError();
