@@ -86,13 +86,17 @@ typedef enum {
  * the payload limit the 1Cat-vLLM page admits to the host path ("Purpose"). */
 #define HR_DEFAULT_MAX_NUMEL 131072u
 
+/* Largest max_numel a channel accepts: 2^29 values = 1 GiB per slot. */
+#define HR_MAX_NUMEL_LIMIT (1ull << 29)
+
 /* Default watchdog for one wait on the peer, in microseconds. */
 #define HR_DEFAULT_TIMEOUT_US 1000000u
 
 typedef struct {
     int device;           /* HIP device ordinal the channel's kernels run on  */
     int world_size;       /* ranks in the group; only 2 is supported          */
-    size_t max_numel;     /* largest numel of one call; 0 = HR_DEFAULT_MAX_NUMEL */
+    size_t max_numel;     /* largest numel of one call; 0 = HR_DEFAULT_MAX_NUMEL;
+                             at most HR_MAX_NUMEL_LIMIT                        */
     int num_blocks;       /* workgroups per rank launch; 0 = automatic.  Both
                              ranks of a loopback channel run at once on one
                              GPU, so the value is clamped to half the device's

@@ -304,7 +304,9 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     if (cfg->world_size != 2) return HR_ERR_UNSUPPORTED;
     if (cfg->device < 0 || cfg->num_blocks < 0) return HR_ERR_INVALID_ARG;
     const size_t max_numel = cfg->max_numel ? cfg->max_numel : HR_DEFAULT_MAX_NUMEL;
-    if (max_numel > (size_t(1) << 30)) return HR_ERR_INVALID_ARG;  // 2 GiB of slots per rank
+    // A slot is addressed by a buffer descriptor whose byte count and
+    // offsets are 32-bit: keep one slot at or below 1 GiB.
+    if (max_numel > HR_MAX_NUMEL_LIMIT) return HR_ERR_INVALID_ARG;
     const uint32_t timeout_us = cfg->timeout_us ? cfg->timeout_us : HR_DEFAULT_TIMEOUT_US;
 
     int ndev = 0;

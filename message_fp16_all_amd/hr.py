@@ -28,6 +28,7 @@ HR_ERR_ABORTED = 7
 
 HR_MAX_G = 16
 HR_DEFAULT_MAX_NUMEL = 131072
+HR_MAX_NUMEL_LIMIT = 1 << 29
 HR_DEFAULT_TIMEOUT_US = 1_000_000
 
 # Every symbol include/hr.h declares.
