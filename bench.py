@@ -77,6 +77,7 @@ class Ctx:
         self.np, self.torch, self.hr, self.inputs = np, torch, hr, inputs
         self.dev = torch.device("cuda", 0)
         self.streams = hr.LoopbackStreams(0)
+        self._streams_w = {2: self.streams}
         self.gate_stream = torch.cuda.Stream()
         self.sleep_rate = None  # sleep-kernel cycles per ms
 
@@ -90,6 +91,16 @@ class Ctx:
 
     def event(self):
         return self.torch.cuda.Event(enable_timing=True)
+
+    def streams_for(self, world):
+        if world not in self._streams_w:
+            self._streams_w[world] = self.hr.LoopbackStreams(0, n=world)
+        return self._streams_w[world]
+
+    def destroy_streams(self):
+        for st in self._streams_w.values():
+            st.destroy()
+        self._streams_w = {}
 
     def calibrate_sleep(self):
         torch = self.torch
@@ -190,86 +201,97 @@ def capture_calls(c: Ctx, ch, rank, xin, out, stream, calls):
     return g
 
 
-def replay_pair(c: Ctx, graphs, gate_ms):
-    """Replay both ranks' graphs behind a common device-side gate; returns
-    (elapsed seconds on the GPU from gate open to both graphs done, host
+def replay_all(c: Ctx, graphs, streams, gate_ms):
+    """Replay every rank's graph behind a common device-side gate; returns
+    (elapsed seconds on the GPU from gate open to all graphs done, host
     submission seconds)."""
     torch = c.torch
-    s0, s1 = c.streams
     torch.cuda.synchronize()
     gate = c.gate(gate_ms)
-    s0.wait_event(gate)
-    s1.wait_event(gate)
-    e0, e1, e_s1 = c.event(), c.event(), torch.cuda.Event()
-    e0.record(s0)
+    for st in streams:
+        st.wait_event(gate)
+    e0, e1 = c.event(), c.event()
+    e0.record(streams[0])
     t_host = time.perf_counter()
-    with torch.cuda.stream(s0):
-        graphs[0].replay()
-    with torch.cuda.stream(s1):
-        graphs[1].replay()
+    for g, st in zip(graphs, streams):
+        with torch.cuda.stream(st):
+            g.replay()
     t_host = time.perf_counter() - t_host
-    e_s1.record(s1)
-    s0.wait_event(e_s1)
-    e1.record(s0)
+    for st in streams[1:]:
+        ev = torch.cuda.Event()
+        ev.record(st)
+        streams[0].wait_event(ev)
+    e1.record(streams[0])
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e-3, t_host
 
 
-def eager_pairs(c: Ctx, ch, x, o, calls):
+def replay_pair(c: Ctx, graphs, gate_ms):
+    return replay_all(c, graphs, c.streams, gate_ms)
+
+
+def eager_calls(c: Ctx, ch, x, o, streams, calls):
     torch = c.torch
-    s0, s1 = c.streams
     torch.cuda.synchronize()
-    e0, e1, e_s1 = c.event(), c.event(), torch.cuda.Event()
-    e0.record(s0)
-    s1.wait_event(e0)
+    e0, e1 = c.event(), c.event()
+    e0.record(streams[0])
+    for st in streams[1:]:
+        st.wait_event(e0)
     for _ in range(calls):
-        ch.allreduce(0, x[0], o[0], s0)
-        ch.allreduce(1, x[1], o[1], s1)
-    e_s1.record(s1)
-    s0.wait_event(e_s1)
-    e1.record(s0)
+        for r, st in enumerate(streams):
+            ch.allreduce(r, x[r], o[r], st)
+    for st in streams[1:]:
+        ev = torch.cuda.Event()
+        ev.record(st)
+        streams[0].wait_event(ev)
+    e1.record(streams[0])
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e-3 / calls
 
 
-def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls=200, gate_ms=None):
+def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=200, gate_ms=None,
+                      world=2):
     torch, hr, inputs = c.torch, c.hr, c.inputs
-    x0b, x1b = inputs.workload2(tokens)
-    n = x0b.size
-    x = [c.to_dev(x0b), c.to_dev(x1b)]
-    o = [torch.empty_like(x[0]), torch.empty_like(x[1])]
-    ref = torch_fold(c, [x0b, x1b])
-    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=5_000_000)
+    xb = inputs.workload2(tokens) if world == 2 else inputs.workload6(world, tokens)
+    n = xb[0].size
+    streams = c.streams_for(world)
+    x = [c.to_dev(b) for b in xb]
+    o = [torch.empty_like(t) for t in x]
+    ref = torch_fold(c, xb)
+    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=5_000_000, world_size=world)
     try:
         for _ in range(warmup):
-            ch.allreduce(0, x[0], o[0], c.streams[0])
-            ch.allreduce(1, x[1], o[1], c.streams[1])
+            for r in range(world):
+                ch.allreduce(r, x[r], o[r], streams[r])
         torch.cuda.synchronize()
-        t_eager = eager_pairs(c, ch, x, o, eager_calls)
-        graphs = [capture_calls(c, ch, r, x[r], o[r], c.streams[r], steps) for r in range(2)]
+        t_eager = eager_calls(c, ch, x, o, streams, eager_calls_n)
+        graphs = [capture_calls(c, ch, r, x[r], o[r], streams[r], steps) for r in range(world)]
         if gate_ms is None:
-            gate_ms = 5.0 + steps * 0.01
+            gate_ms = 5.0 + steps * 0.01 * world / 2
         for _ in range(2):                       # upload + settle, untimed
-            replay_pair(c, graphs, gate_ms)
-        o[0].zero_()
-        o[1].zero_()
+            replay_all(c, graphs, streams, gate_ms)
+        for t in o:
+            t.zero_()
         torch.cuda.synchronize()
-        elapsed, host_s = replay_pair(c, graphs, gate_ms)
+        elapsed, host_s = replay_all(c, graphs, streams, gate_ms)
         if ch.status() != hr.HR_OK:
             raise RuntimeError(f"exchange failed: {hr.hr_status_str(ch.status())}")
         got0 = c.to_host(o[0])
-        exact = same(c.np, got0, ref) and same(c.np, c.to_host(o[1]), ref)
+        exact = all(same(c.np, c.to_host(t), ref) for t in o)
         del graphs
         torch.cuda.synchronize()
     finally:
         ch.destroy()
     t_graph = elapsed / steps
-    alg = 3 * n * 2
+    alg = (world + 1) * n * 2
+    d2h = world * n * 2                 # each rank publishes its slice once
+    h2d = world * (world - 1) * n * 2   # each rank reads every peer's slice
     return {
-        "tokens": tokens, "N": n, "bytes_per_call": alg,
+        "world": world, "tokens": tokens, "N": n, "bytes_per_call": alg,
         "graph_us": round(t_graph * 1e6, 3), "graph_GBps": round(alg / t_graph / 1e9, 2),
         "graph_frac_link": round(alg / t_graph / 1e9 / link_peak, 4),
-        "link_GBps_per_dir": round(2 * n * 2 / t_graph / 1e9, 2),
+        "link_GBps_per_dir": round(max(d2h, h2d) / t_graph / 1e9, 2),
+        "link_busiest_dir_frac": round(max(d2h, h2d) / t_graph / 1e9 / link_peak, 4),
         "eager_us": round(t_eager * 1e6, 3), "eager_GBps": round(alg / t_eager / 1e9, 2),
         "eager_frac_link": round(alg / t_eager / 1e9 / link_peak, 4),
         "graph_calls": steps, "gate_ms": gate_ms, "host_submit_ms": round(host_s * 1e3, 3),
@@ -610,6 +632,15 @@ def main():
                 r.pop("_out")
                 rows.append(r)
             cfgs["exchange_2rank_host_slots"] = rows
+            rows = []
+            for w in (4, 8):
+                for t in (1, 8, 32):
+                    log(f"exchange world={w} tokens={t}")
+                    r = exchange_workload(c, t, 300, 20, link_peak, eager_calls_n=50, world=w)
+                    r.pop("_elapsed_s")
+                    r.pop("_out")
+                    rows.append(r)
+            cfgs["exchange_world_host_slots"] = rows
         if want("c5"):
             log("exchange graph of 1000 fresh calls, N=10240")
             cfgs["exchange_graph_1000_calls_N10240"] = workload5(c, link_peak)
@@ -626,7 +657,7 @@ def main():
         log("CPU oracle baseline")
         cpu = cpu_baseline(c, args.tokens, head_out)
 
-    c.streams.destroy()
+    c.destroy_streams()
     t_call = elapsed / args.steps
     n = head["N"]
     alg = 3 * n * 2

@@ -23,16 +23,16 @@
  *  - hr_reduce_f16: G contributions already resident in device memory (HBM)
  *    are folded into one output buffer by one kernel launch.
  *
- *  - hr_allreduce_f16: a two-rank exchange through a channel.  Each rank's
- *    kernel writes its contribution into pinned, device-mapped host memory,
- *    raises a per-workgroup ready flag, waits for the peer's flag and adds
- *    the peer's values, exactly as the 1Cat-vLLM page's "Purpose" section
- *    lays out: one kernel per call, no CPU work, no stream synchronisation,
- *    so the call can be captured into a hipGraph; host slots are double
- *    buffered by call parity.  The channel is a handle so that one process
- *    can own several two-rank groups (same section).  Both ranks of a
- *    channel may live in one process on one GPU ("loopback": two
- *    concurrently running launches on two streams).
+ *  - hr_allreduce_f16: an exchange through a channel of W ranks (W = 2 is
+ *    the two-rank method; up to HR_MAX_WORLD).  Each rank's kernel writes
+ *    its contribution into pinned, device-mapped host memory, raises a
+ *    per-workgroup ready flag, waits for the peers' flags and adds the
+ *    peers' values, as the 1Cat-vLLM page's "Purpose" section lays out: one
+ *    kernel per call, no CPU work, no stream synchronisation, so the call can
+ *    be captured into a hipGraph; host slots are double buffered by call
+ *    parity.  The channel is a handle so that one process can own several
+ *    groups (same section).  All ranks of a channel may live in one process
+ *    on one GPU ("loopback": concurrently running launches on W streams).
  *
  * Conventions for every function:
  *  - Every function returns an hr_status; nothing throws across the ABI.
@@ -73,7 +73,7 @@ typedef enum {
     HR_ERR_INVALID_ARG = 1,  /* null pointer, bad rank/G, partial overlap  */
     HR_ERR_ALIGNMENT = 2,    /* a binary16 pointer that is not 2-byte aligned */
     HR_ERR_TOO_LARGE = 3,    /* numel above the channel's max_numel          */
-    HR_ERR_UNSUPPORTED = 4,  /* world_size other than 2, device unusable     */
+    HR_ERR_UNSUPPORTED = 4,  /* world_size outside 2..HR_MAX_WORLD, device unusable */
     HR_ERR_HIP = 5,          /* a HIP runtime call failed                    */
     HR_ERR_TIMEOUT = 6,      /* a wait for the peer exceeded timeout_us      */
     HR_ERR_ABORTED = 7       /* hr_channel_abort cancelled waiting kernels   */
@@ -81,6 +81,9 @@ typedef enum {
 
 /* Largest number of contributions hr_reduce_f16 folds in one call. */
 #define HR_MAX_G 16
+
+/* Largest group a channel serves. */
+#define HR_MAX_WORLD 8
 
 /* Default cap of one exchange: 131072 binary16 values = 256 KiB per rank,
  * the payload limit the 1Cat-vLLM page admits to the host path ("Purpose"). */
@@ -94,13 +97,15 @@ typedef enum {
 
 typedef struct {
     int device;           /* HIP device ordinal the channel's kernels run on  */
-    int world_size;       /* ranks in the group; only 2 is supported          */
+    int world_size;       /* ranks W in the group, 2..HR_MAX_WORLD; 2 is the
+                             source's two-rank method, larger W folds all
+                             ranks left in rank order                         */
     size_t max_numel;     /* largest numel of one call; 0 = HR_DEFAULT_MAX_NUMEL;
                              at most HR_MAX_NUMEL_LIMIT                        */
-    int num_blocks;       /* workgroups per rank launch; 0 = automatic.  Both
+    int num_blocks;       /* workgroups per rank launch; 0 = automatic.  All
                              ranks of a loopback channel run at once on one
-                             GPU, so the value is clamped to half the device's
-                             compute units.                                    */
+                             GPU, so the value is clamped to the device's
+                             compute units / world_size.                       */
     uint32_t timeout_us;  /* watchdog per wait; 0 = HR_DEFAULT_TIMEOUT_US      */
 } hr_channel_config;
 
@@ -113,7 +118,7 @@ typedef struct {
     int block_threads;            /* threads per workgroup of one launch      */
     uint32_t timeout_us;
     void *host_slots;             /* host address of the slot region:
-                                     [2 parity][2 rank][slot_stride] binary16 */
+                                     [2 parity][world][slot_stride] binary16  */
     size_t slot_stride;           /* elements per slot (>= max_numel)         */
     volatile uint32_t *host_flags; /* host address of the ready flags:
                                      flag of (rank r, block b) at index
@@ -124,10 +129,10 @@ typedef struct {
 } hr_channel_info;
 
 /*
- * hr_create_channel -- set up one two-rank exchange group.
+ * hr_create_channel -- set up one exchange group of world_size ranks.
  *
  * Allocates the channel's pinned, device-mapped, fine-grained host memory
- * (slots [2 parity][2 rank][max_numel] binary16, per-workgroup ready flags,
+ * (slots [2 parity][world][max_numel] binary16, per-workgroup ready flags,
  * the error and abort words) and its device-resident per-workgroup call
  * counters, and zeroes them.  The slot region has the 2 x world_size x
  * max_numel shape of the double-buffered workspace that the SGLang page's
@@ -137,29 +142,32 @@ typedef struct {
  * cfg:  see hr_channel_config.  *out receives the handle on success and is
  *       left untouched on failure.
  * Errors: HR_ERR_INVALID_ARG (null cfg/out, negative or out-of-range
- *       fields), HR_ERR_UNSUPPORTED (world_size != 2), HR_ERR_HIP.
+ *       fields), HR_ERR_UNSUPPORTED (world_size outside 2..HR_MAX_WORLD),
+ *       HR_ERR_HIP.
  */
 HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out);
 
 /*
- * hr_allreduce_f16 -- one two-rank all-reduce call of rank `rank`.
+ * hr_allreduce_f16 -- one all-reduce call of rank `rank` (0..world_size-1).
  *
  * Enqueues exactly one kernel on `stream`.  Its workgroups each own one
  * contiguous slice of the numel values: they copy the slice of `in` into this
- * rank's host slot of the current parity, fence at system scope, raise their
- * ready flag, wait (watchdog-bounded) for the peer's flag of the same call,
- * read the peer's slice from its host slot and write fl16(x0 + x1) -- rank 0's
- * value first -- to `out` (1Cat-vLLM page, "Purpose").  Parity comes from a
- * device-resident per-workgroup call counter, so a replayed graph alternates
- * slots without host involvement.
+ * rank's host slot of the current parity, make the stores visible at system
+ * scope, raise their ready flag, wait (watchdog-bounded) for every peer's
+ * flag of the same call, read the peers' slices from their host slots and
+ * write the left fold x0 + x1 + ... in rank order, one binary16 rounding per
+ * add, to `out` (for two ranks fl16(x0 + x1), the 1Cat-vLLM page's
+ * "Purpose").  Parity comes from a device-resident per-workgroup call
+ * counter, so a replayed graph alternates slots without host involvement.
  *
  * in, out: device binary16 buffers of numel values; out == in is allowed,
  *          any other overlap is an error.
  * numel:   0 enqueues nothing; must not exceed the channel's max_numel.
- * Both ranks must issue the same sequence of numel values.  Rank 0 and rank
- * 1 must be driven from streams that can run concurrently (two processes, or
- * two non-blocking streams of one process), each endpoint by one stream at a
- * time; both launches must be in flight together or the waits time out.
+ * All ranks must issue the same sequence of numel values.  The ranks must be
+ * driven from streams that can run concurrently (separate processes, or, in
+ * one process, streams from hr_loopback_stream_create), each endpoint by one
+ * stream at a time; all launches of a call must be in flight together or the
+ * waits time out.
  *
  * Errors: HR_ERR_INVALID_ARG, HR_ERR_ALIGNMENT, HR_ERR_TOO_LARGE (the caller
  * keeps its own collective for larger payloads), HR_ERR_HIP; and the
@@ -216,7 +224,8 @@ HR_API hr_status hr_destroy(hr_channel ch);
 /*
  * hr_loopback_stream_create -- a stream for one rank of a loopback channel.
  *
- * The two launches of one exchange call must run at the same time.  The HIP
+ * The launches of one exchange call (one per rank) must run at the same
+ * time.  The HIP
  * runtime spreads ordinary streams over a small pool of hardware queues
  * (GPU_MAX_HW_QUEUES), and two streams that share a queue run their kernels
  * one after the other, so ordinary streams give no such guarantee.  A stream
@@ -224,7 +233,7 @@ HR_API hr_status hr_destroy(hr_channel ch);
  * compute-unit mask (the runtime never pools such queues) that enables every
  * compute unit of `device`.  It is ordered with the null stream like any
  * stream created without hipStreamNonBlocking, so do not enqueue work on the
- * null stream between the two ranks' launches of one call.
+ * null stream between the ranks' launches of one call.
  *
  * device: HIP device ordinal.  *out receives a hipStream_t owned by the
  * caller, released with hr_loopback_stream_destroy.

@@ -1,28 +1,33 @@
-// exchange.hip -- the two-rank FP16 all-reduce through pinned host slots.
+// exchange.hip -- the FP16 all-reduce of a W-rank group through pinned
+// host slots (W = 2 is the method of the source; 3..8 extend it).
 //
 // The method is the one the 1Cat-vLLM pull request "[Kernel] Two-rank FP16
 // all-reduce through pinned host memory for GPUs without P2P" lays out in
 // its "Purpose" section: one kernel per call; each workgroup writes its chunk
-// of the rank's contribution into host memory that both ranks map, fences,
-// raises a per-workgroup ready flag, waits for the peer's flag and adds the
-// peer's chunk with a single FP16 rounding, so both ranks obtain the same
+// of the rank's contribution into host memory that the ranks map, fences,
+// raises a per-workgroup ready flag, waits for the peers' flags and adds the
+// peers' chunks, one FP16 rounding per add, so every rank obtains the same
 // bits; there is no CPU work and no stream synchronisation, so the call can
 // be captured into a graph, and the host slots are double buffered by call
 // parity.  Channels are handles so one process can own several groups (same
-// section).
+// section).  For W > 2 the values are folded left in rank order 0..W-1 (the
+// SGLang pull request "[SM120] Add optional FlashInfer PCIe-IPC all-reduce
+// for switch-free hosts", section "Accuracy", shows that order changes bits).
 //
 // Channel memory
 //   host (pinned, device-mapped, fine-grained/coherent):
-//     slots  [2 parity][2 rank][stride] binary16
-//     flags  [2 rank][nblocks], one 128-byte line each: the call number of
+//     slots  [2 parity][W rank][stride] binary16 -- the 2 x world x numel
+//            workspace of the SGLang page's "Modifications" section
+//     flags  [W rank][nblocks], one 128-byte line each: the call number of
 //            the last chunk that workgroup published
 //     error word, abort word (one line each)
-//   device (HBM): epoch[2 rank][nblocks] -- per-workgroup call counter,
+//   device (HBM): epoch[W rank][nblocks] -- per-workgroup call counter,
 //     device error word.
 //
 // Every launch has the channel's fixed workgroup count; each workgroup
 // advances its call counter, so parity is uniform across a call.  Only the
-// first `nactive` workgroups (a function of numel, so equal on both ranks)
+// first `nactive` workgroups (a function of numel and W, so equal on every
+// rank)
 // carry values and take part in the flag handshake: fewer pollers means less
 // non-posted traffic on the host link, which is what bounds small calls.
 //
@@ -32,17 +37,18 @@
 //   2. every lane waits for its stores to be acknowledged; barrier; lane 0
 //      stores flag[r][b] = e at system scope -- the "fence, then flag" of
 //      the method, without a whole-cache write-back
-//   3. lane 0 polls flag[peer][b] with system-scope loads until it reaches
-//      e (wrap-safe signed compare, so a peer already at e + 1 also
-//      releases the wait), sleeping between polls; it also polls the abort
-//      word and a watchdog on the constant-rate wall clock
-//   4. barrier, then system-coherent loads of slot[e & 1][peer] (H2D) and
-//      plain loads of its own slice of `in` again; store fl16(x0 + x1)
-//      with rank 0's value first to `out`.
-// Why one parity cannot be overwritten while the peer still reads it: a
-// rank starts call e + 2 (same parity as e) only after its call e + 1 has
-// finished, and in call e + 1 its workgroup 0 (always active) waited for the
-// peer's flag of call e + 1, which the peer raises only after its whole
+//   3. lanes q != r of the first wave poll flag[q][b] with system-scope
+//      loads until each reaches e (wrap-safe signed compare, so a peer
+//      already at e + 1 also releases the wait), sleeping between polls;
+//      lane 0 also polls the abort word, and a watchdog on the
+//      constant-rate wall clock bounds the wait
+//   4. barrier, then system-coherent loads of slot[e & 1][q] for every
+//      peer q (H2D) and plain loads of its own slice of `in` again; store
+//      the left fold x0 + x1 + ... + x_{W-1}, in rank order, to `out`.
+// Why one parity cannot be overwritten while a peer still reads it: a rank
+// starts call e + 2 (same parity as e) only after its call e + 1 has
+// finished, and in call e + 1 its workgroup 0 (always active) waited for
+// every peer's flag of call e + 1, which a peer raises only after its whole
 // call-e kernel has finished (stream order).
 //
 // Errors (timeout, abort) are written to the device error word and the
@@ -60,8 +66,9 @@
 namespace hr {
 
 constexpr int kExchThreads = 256;
-constexpr int kExchUnroll = 4;
-constexpr int kMinActive = 8;
+constexpr int kExchUnroll = 4;                    // units per lane per publish batch
+constexpr int kMaxWorld = 8;
+constexpr int kMinActivePolls = 16;                // W * minimum active workgroups
 constexpr size_t kLine = 128;                     // bytes per flag / word line
 constexpr size_t kFlagStride = kLine / sizeof(uint32_t);
 
@@ -78,12 +85,19 @@ struct ExchArgs {
     const uint32_t *abort_w;  // device view of the host abort word
     uint64_t timeout_ticks;
     int rank;
+    int world;
     int nblocks;   // launched workgroups (the channel's fixed count)
     int nactive;   // workgroups that carry values in this call
 };
 
 __device__ __forceinline__ u32x4 combine(u32x4 x0, u32x4 x1) { return add_f16x8(x0, x1); }
 __device__ __forceinline__ uint16_t combine(uint16_t x0, uint16_t x1) { return add_f16x1(x0, x1); }
+
+// Units per lane per combine batch: W loads each, at most 8 in flight.
+template <int W>
+struct CombineShape {
+    static constexpr int U = (8 / W) > 0 ? (8 / W) : 1;
+};
 
 // Host-slot accesses are buffer loads/stores with the system-coherence bits
 // (sc0 sc1): stores write through every GPU cache level to host memory and
@@ -125,12 +139,12 @@ struct HostIO<uint16_t> {
 // Workgroup b of an active set of `nact` owns the 8-value units
 // [nvec*b/nact, nvec*(b+1)/nact) of the call, nvec = numel / 8, and the last
 // active workgroup also owns the numel % 8 trailing values.  The split
-// depends on numel alone, so workgroup b covers the same values on both
-// ranks whichever access path (16-byte or 2-byte) each rank takes.
+// depends on numel alone, so workgroup b covers the same values on every
+// rank whichever access path (16-byte or 2-byte) each rank takes.
 //
-// VEC selects the lane access unit: one 16-byte unit (all buffers 16-byte
-// aligned) or one value (2-byte aligned buffers).
-template <bool VEC>
+// W is the group size; VEC selects the lane access unit: one 16-byte unit
+// (all buffers 16-byte aligned) or one value (2-byte aligned buffers).
+template <int W, bool VEC>
 __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
     __shared__ uint32_t s_epoch;
     __shared__ uint32_t s_status;
@@ -150,7 +164,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
     if (s_status != 0 || b >= a.nactive) return;
     const uint32_t e = s_epoch;
     const int parity = static_cast<int>(e & 1u);
-    const int peer = a.rank ^ 1;
+    const int rank = a.rank;
 
     const size_t nvec = a.numel / kVecElems;
     const size_t lo = nvec * static_cast<size_t>(b) / static_cast<size_t>(a.nactive);
@@ -163,10 +177,10 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
     const size_t ulo = lo * (kVecElems / per), uhi = hi * (kVecElems / per);
     const T *in = static_cast<const T *>(a.in);
     T *out = static_cast<T *>(a.out);
-    const __amdgpu_buffer_rsrc_t mine =
-        slot_rsrc(a.slots + static_cast<size_t>(2 * parity + a.rank) * a.stride, a.stride);
-    const __amdgpu_buffer_rsrc_t theirs =
-        slot_rsrc(a.slots + static_cast<size_t>(2 * parity + peer) * a.stride, a.stride);
+    __amdgpu_buffer_rsrc_t slot[W];
+#pragma unroll
+    for (int q = 0; q < W; ++q)
+        slot[q] = slot_rsrc(a.slots + static_cast<size_t>(W * parity + q) * a.stride, a.stride);
 
     // 1. publish this rank's slice into its host slot (write-through)
     for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
@@ -179,28 +193,36 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
 #pragma unroll
         for (int u = 0; u < kExchUnroll; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < uhi) HostIO<T>::store(mine, v, x[u]);
+            if (v < uhi) HostIO<T>::store(slot[rank], v, x[u]);
         }
     }
     if (last && tail0 + tid < a.numel)
-        HostIO<uint16_t>::store(mine, tail0 + tid, static_cast<const uint16_t *>(a.in)[tail0 + tid]);
+        HostIO<uint16_t>::store(slot[rank], tail0 + tid, static_cast<const uint16_t *>(a.in)[tail0 + tid]);
 
     // 2. every lane waits until its slot stores are acknowledged, so they
     //    are in host memory before lane 0 raises the flag
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    // 3. raise this workgroup's flag, then wait for the peer's
-    if (tid == 0) {
-        __hip_atomic_store(a.flags + (static_cast<size_t>(a.rank) * a.nblocks + b) * kFlagStride, e,
+    if (tid == 0)
+        __hip_atomic_store(a.flags + (static_cast<size_t>(rank) * a.nblocks + b) * kFlagStride, e,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        const uint32_t *pf = a.flags + (static_cast<size_t>(peer) * a.nblocks + b) * kFlagStride;
+
+    // 3. the first wave waits for every peer's flag, one lane per peer
+    if (tid < 64) {
+        const bool polls = tid < W && tid != rank;
+        const uint32_t *pf = a.flags + (static_cast<size_t>(polls ? tid : 0) * a.nblocks + b) * kFlagStride;
+        bool done = !polls;
         uint32_t status = 0;
         const long long t0 = wall_clock64();
         for (;;) {
-            const uint32_t f = __hip_atomic_load(pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            if (static_cast<int32_t>(f - e) >= 0) break;
-            if (__hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) {
+            if (!done) {
+                const uint32_t f = __hip_atomic_load(pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                done = static_cast<int32_t>(f - e) >= 0;
+            }
+            if (__all(done)) break;
+            uint32_t ab = 0;
+            if (tid == 0) ab = __hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (__shfl(ab, 0) != 0) {
                 status = HR_ERR_ABORTED;
                 break;
             }
@@ -210,51 +232,87 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        if (status != 0) {
-            __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.host_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (tid == 0) {
+            if (status != 0) {
+                __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.host_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+            s_status = status;
         }
-        s_status = status;
     }
-    // the barrier orders every lane's slot loads after the flag lane 0 saw;
-    // the loads themselves read host memory, not a cached copy
+    // the barrier orders every lane's slot loads after the flags the first
+    // wave saw; the loads themselves read host memory, not a cached copy
     __syncthreads();
     if (s_status != 0) return;
 
-    // 4. combine in rank order: x0 + x1
-    for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
-        T y[kExchUnroll], x[kExchUnroll];
+    // 4. combine: left fold in rank order x0 + x1 + ... + x_{W-1}
+    constexpr int UC = CombineShape<W>::U;
+    for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * UC) {
+        T x[W][UC];
 #pragma unroll
-        for (int u = 0; u < kExchUnroll; ++u) {
+        for (int u = 0; u < UC; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
             if (v < uhi) {
-                y[u] = HostIO<T>::load(theirs, v);
-                x[u] = in[v];
+#pragma unroll
+                for (int q = 0; q < W; ++q) x[q][u] = (q == rank) ? in[v] : HostIO<T>::load(slot[q], v);
             }
         }
 #pragma unroll
-        for (int u = 0; u < kExchUnroll; ++u) {
+        for (int u = 0; u < UC; ++u) {
             const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < uhi) out[v] = (a.rank == 0) ? combine(x[u], y[u]) : combine(y[u], x[u]);
+            if (v < uhi) {
+                T acc = x[0][u];
+#pragma unroll
+                for (int q = 1; q < W; ++q) acc = combine(acc, x[q][u]);
+                out[v] = acc;
+            }
         }
     }
     if (last && tail0 + tid < a.numel) {
-        const uint16_t xv = static_cast<const uint16_t *>(a.in)[tail0 + tid];
-        const uint16_t yv = HostIO<uint16_t>::load(theirs, tail0 + tid);
-        static_cast<uint16_t *>(a.out)[tail0 + tid] = (a.rank == 0) ? add_f16x1(xv, yv) : add_f16x1(yv, xv);
+        const size_t i = tail0 + tid;
+        uint16_t acc = 0;
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            const uint16_t xq = (q == rank) ? static_cast<const uint16_t *>(a.in)[i] : HostIO<uint16_t>::load(slot[q], i);
+            acc = (q == 0) ? xq : add_f16x1(acc, xq);
+        }
+        static_cast<uint16_t *>(a.out)[i] = acc;
     }
 }
 
 // Active workgroups for a call of numel values: about one 16-byte unit per
-// lane, at least kMinActive (so small calls still spread their flag traffic
-// over a few workgroups), at most the channel's workgroup count.  A function
-// of numel alone, so both ranks agree.
-inline int active_blocks(size_t numel, int nblocks) {
+// lane, at least 16 / W (so small calls still spread their flag traffic over
+// a few workgroups, while large groups, whose every workgroup polls W - 1
+// flags, keep the pollers few), at most the channel's workgroup count.  A
+// function of numel and W alone, so every rank agrees.
+inline int active_blocks(size_t numel, int nblocks, int world) {
     const size_t nvec = numel / kVecElems;
     size_t want = (nvec + kExchThreads - 1) / kExchThreads;
-    if (want < static_cast<size_t>(kMinActive)) want = kMinActive;
+    const size_t floor_ = static_cast<size_t>(kMinActivePolls / world > 0 ? kMinActivePolls / world : 1);
+    if (want < floor_) want = floor_;
     if (want > static_cast<size_t>(nblocks)) want = static_cast<size_t>(nblocks);
     return static_cast<int>(want);
+}
+
+template <int W>
+void launch_exchange(const ExchArgs &a, bool vec, hipStream_t s) {
+    if (vec)
+        hipLaunchKernelGGL((exchange_f16<W, true>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((exchange_f16<W, false>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+}
+
+inline void launch_exchange_w(const ExchArgs &a, bool vec, hipStream_t s) {
+    switch (a.world) {
+        case 2: launch_exchange<2>(a, vec, s); break;
+        case 3: launch_exchange<3>(a, vec, s); break;
+        case 4: launch_exchange<4>(a, vec, s); break;
+        case 5: launch_exchange<5>(a, vec, s); break;
+        case 6: launch_exchange<6>(a, vec, s); break;
+        case 7: launch_exchange<7>(a, vec, s); break;
+        case 8: launch_exchange<8>(a, vec, s); break;
+        default: break;
+    }
 }
 
 }  // namespace hr
@@ -272,7 +330,7 @@ struct hr_channel_s {
     void *host_base;           // hipHostMalloc'ed region (host address)
     unsigned char *host_dev;   // the same region as seen by the device
     size_t flags_off, error_off, abort_off, host_bytes;
-    uint32_t *dev_words;       // hipMalloc: epochs[2 * nblocks] then the error word
+    uint32_t *dev_words;       // hipMalloc: epochs[world * nblocks] then the error word
 };
 
 namespace {
@@ -301,7 +359,7 @@ void release(hr_channel ch) {
 
 extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out) {
     if (cfg == nullptr || out == nullptr) return HR_ERR_INVALID_ARG;
-    if (cfg->world_size != 2) return HR_ERR_UNSUPPORTED;
+    if (cfg->world_size < 2 || cfg->world_size > kMaxWorld) return HR_ERR_UNSUPPORTED;
     if (cfg->device < 0 || cfg->num_blocks < 0) return HR_ERR_INVALID_ARG;
     const size_t max_numel = cfg->max_numel ? cfg->max_numel : HR_DEFAULT_MAX_NUMEL;
     // A slot is addressed by a buffer descriptor whose byte count and
@@ -324,30 +382,31 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     hr_channel ch = new (std::nothrow) hr_channel_s{};
     if (ch == nullptr) return HR_ERR_HIP;
     ch->device = cfg->device;
-    ch->world_size = 2;
+    const int world = cfg->world_size;
+    ch->world_size = world;
     ch->max_numel = max_numel;
     ch->stride = round_up(max_numel, kLine / sizeof(uint16_t));
-    // Default: half of the compute units per rank, so that both ranks of a
+    // Default and ceiling: CUs / world per rank, so that all ranks of a
     // loopback channel are resident at once.
-    int nb = cfg->num_blocks ? cfg->num_blocks : cus / 2;
-    if (nb > cus / 2) nb = cus / 2;
+    int nb = cfg->num_blocks ? cfg->num_blocks : cus / world;
+    if (nb > cus / world) nb = cus / world;
     if (nb < 1) nb = 1;
     ch->nblocks = nb;
     ch->timeout_us = timeout_us;
     ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
 
-    const size_t slot_bytes = 4 * ch->stride * sizeof(uint16_t);
+    const size_t slot_bytes = 2 * static_cast<size_t>(world) * ch->stride * sizeof(uint16_t);
     ch->flags_off = round_up(slot_bytes, kLine);
-    ch->error_off = ch->flags_off + 2 * static_cast<size_t>(nb) * kLine;
+    ch->error_off = ch->flags_off + static_cast<size_t>(world) * static_cast<size_t>(nb) * kLine;
     ch->abort_off = ch->error_off + kLine;
     ch->host_bytes = ch->abort_off + kLine;
 
     void *dev_view = nullptr;
     if (hipHostMalloc(&ch->host_base, ch->host_bytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
         hipHostGetDevicePointer(&dev_view, ch->host_base, 0) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void **>(&ch->dev_words), (2 * static_cast<size_t>(nb) + 1) * sizeof(uint32_t)) !=
-            hipSuccess ||
-        hipMemset(ch->dev_words, 0, (2 * static_cast<size_t>(nb) + 1) * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&ch->dev_words),
+                  (static_cast<size_t>(world) * nb + 1) * sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(ch->dev_words, 0, (static_cast<size_t>(world) * nb + 1) * sizeof(uint32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         release(ch);
         return HR_ERR_HIP;
@@ -361,7 +420,7 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
 
 extern "C" HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void *in, void *out, size_t numel,
                                              hr_stream_t stream) {
-    if (ch == nullptr || (rank != 0 && rank != 1)) return HR_ERR_INVALID_ARG;
+    if (ch == nullptr || rank < 0 || rank >= ch->world_size) return HR_ERR_INVALID_ARG;
     const uint32_t sticky = __atomic_load_n(
         reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->error_off), __ATOMIC_ACQUIRE);
     if (sticky != 0) return static_cast<hr_status>(sticky);
@@ -383,19 +442,16 @@ extern "C" HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void
     a.stride = ch->stride;
     a.flags = reinterpret_cast<uint32_t *>(ch->host_dev + ch->flags_off);
     a.epochs = ch->dev_words + static_cast<size_t>(rank) * ch->nblocks;
-    a.dev_error = ch->dev_words + 2 * static_cast<size_t>(ch->nblocks);
+    a.dev_error = ch->dev_words + static_cast<size_t>(ch->world_size) * ch->nblocks;
     a.host_error = reinterpret_cast<uint32_t *>(ch->host_dev + ch->error_off);
     a.abort_w = reinterpret_cast<const uint32_t *>(ch->host_dev + ch->abort_off);
     a.timeout_ticks = ch->timeout_ticks;
     a.rank = rank;
+    a.world = ch->world_size;
     a.nblocks = ch->nblocks;
-    a.nactive = active_blocks(numel, ch->nblocks);
+    a.nactive = active_blocks(numel, ch->nblocks, ch->world_size);
 
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (aligned(in, 16) && aligned(out, 16))
-        hipLaunchKernelGGL(exchange_f16<true>, dim3(ch->nblocks), dim3(kExchThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(exchange_f16<false>, dim3(ch->nblocks), dim3(kExchThreads), 0, s, a);
+    launch_exchange_w(a, aligned(in, 16) && aligned(out, 16), reinterpret_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
 }
 

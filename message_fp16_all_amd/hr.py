@@ -27,6 +27,7 @@ HR_ERR_TIMEOUT = 6
 HR_ERR_ABORTED = 7
 
 HR_MAX_G = 16
+HR_MAX_WORLD = 8
 HR_DEFAULT_MAX_NUMEL = 131072
 HR_MAX_NUMEL_LIMIT = 1 << 29
 HR_DEFAULT_TIMEOUT_US = 1_000_000
@@ -197,11 +198,13 @@ def reduce(tensors, out, stream=None):
 
 
 class Channel:
-    """An owned two-rank channel; ``allreduce`` enqueues one rank's call."""
+    """An owned channel of ``world_size`` ranks; ``allreduce`` enqueues one
+    rank's call."""
 
     def __init__(self, device: int = 0, max_numel: int = 0, num_blocks: int = 0,
-                 timeout_us: int = 0):
-        self.handle = hr_create_channel(device, 2, max_numel, num_blocks, timeout_us)
+                 timeout_us: int = 0, world_size: int = 2):
+        self.world_size = world_size
+        self.handle = hr_create_channel(device, world_size, max_numel, num_blocks, timeout_us)
 
     def allreduce(self, rank: int, inp, out, stream=None):
         n = inp.numel()
@@ -234,12 +237,12 @@ class Channel:
 
 
 class LoopbackStreams:
-    """Two streams for the two ranks of a loopback channel, each owning its
-    hardware queue (see hr_loopback_stream_create), wrapped as torch streams."""
+    """One stream per rank of a loopback channel, each owning its hardware
+    queue (see hr_loopback_stream_create), wrapped as torch streams."""
 
-    def __init__(self, device: int = 0):
+    def __init__(self, device: int = 0, n: int = 2):
         import torch
-        self.handles = [hr_loopback_stream_create(device), hr_loopback_stream_create(device)]
+        self.handles = [hr_loopback_stream_create(device) for _ in range(n)]
         self.streams = tuple(torch.cuda.ExternalStream(h, device=torch.device("cuda", device))
                              for h in self.handles)
 
@@ -250,7 +253,7 @@ class LoopbackStreams:
         return iter(self.streams)
 
     def __len__(self):
-        return 2
+        return len(self.streams)
 
     def destroy(self):
         for s in self.streams:

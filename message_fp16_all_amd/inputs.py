@@ -25,7 +25,9 @@ no data, so seeded Gaussians of those shapes are used:
 * workload 4 -- eight ranks, 2048 tokens x hidden 8192 = 16777216 values
   each (32 MiB per rank, one prefill chunk), sigma 1;
 * workload 5 -- two-rank exchange repeated over 1000 calls, 10240 values per
-  rank per call (batch 2 x hidden 5120), fresh sigma-1 values per call.
+  rank per call (batch 2 x hidden 5120), fresh sigma-1 values per call;
+* workload 6 -- exchange among W = 3..8 ranks (the SGLang page's world sizes
+  4 and 8), 4096 x tokens values per rank, sigma 0.5, independent per rank.
 
 ``edge_pairs`` adds every ordered pair of 17 special values (signed zeros,
 subnormal extremes, the smallest normal, one, 2048, the largest finite, the
@@ -46,6 +48,7 @@ WORKLOADS = {
     3: dict(G=8, n=393_216, sigma=0.1),
     4: dict(G=8, n=16_777_216, sigma=1.0),
     5: dict(G=2, n=10_240, sigma=1.0, calls=1000),
+    6: dict(sigma=0.5),
 }
 
 EDGE_VALUES = np.array([
@@ -130,6 +133,12 @@ def workload5(calls: int | None = None, n: int | None = None) -> np.ndarray:
         for c in range(calls):
             out[r, c] = gaussian(n, w["sigma"], 5, r, c)
     return out
+
+
+def workload6(world: int, tokens: int, call: int = 0):
+    """`world` contributions of 4096 * tokens values for a W-rank exchange."""
+    n = HIDDEN_DECODE * tokens
+    return [gaussian(n, WORKLOADS[6]["sigma"], 6, r, call) for r in range(world)]
 
 
 def edge_pairs():

@@ -85,7 +85,7 @@ def test_channel_validation_before_any_device_call():
     lib = hr.load()
     h = ctypes.c_void_p()
     assert lib.hr_create_channel(None, ctypes.byref(h)) == hr.HR_ERR_INVALID_ARG
-    for ws in (1, 3, 8):
+    for ws in (0, 1, 9, 16):
         cfg = hr.hr_channel_config(0, ws, 0, 0, 0)
         assert lib.hr_create_channel(ctypes.byref(cfg), ctypes.byref(h)) == hr.HR_ERR_UNSUPPORTED
     cfg = hr.hr_channel_config(-1, 2, 0, 0, 0)

@@ -259,9 +259,9 @@ def test_host_acts_as_the_peer(streams):
         seen = np.frombuffer(ctypes.string_at(own_slot, n * 2), dtype=np.uint16)
         assert np.array_equal(seen, x0b)
         # workgroups that carried values raised their flag for call 1; the
-        # idle ones (about one 16-byte unit per lane, at least 8 active)
-        # never touch the flags
-        active = min(info.num_blocks, max(8, -(-(n // 8) // info.block_threads)))
+        # idle ones never touch the flags (active: about one 16-byte unit per
+        # lane, at least 16 / W = 8 for two ranks)
+        active = min(info.num_blocks, max(16 // 2, -(-(n // 8) // info.block_threads)))
         raised = [info.host_flags[(0 * info.num_blocks + b) * info.flag_stride]
                   for b in range(info.num_blocks)]
         assert raised == [1] * active + [0] * (info.num_blocks - active)
