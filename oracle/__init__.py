@@ -14,8 +14,9 @@ Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The product library and its Python binding never do,
 and nothing here imports them.
 
-Arrays cross this boundary as numpy ``uint16`` bit patterns (binary16 bits),
-never as numpy ``float16`` values, so that no numpy arithmetic is involved.
+Arrays cross this boundary as numpy ``uint16`` bit patterns (binary16 or
+bfloat16 bits), never as numpy float values, so that no numpy arithmetic is
+involved.  The ``*_bf16`` functions are the same combine on bfloat16.
 """
 from __future__ import annotations
 
@@ -61,6 +62,14 @@ def _bind(path: str):
     lib.hro_fold_threads.argtypes = [ctypes.POINTER(u16p), ctypes.c_int, ctypes.c_size_t,
                                      u16p, ctypes.c_int]
     lib.hro_fold_threads.restype = ctypes.c_int
+    lib.hro_decode_bf16_vec.argtypes = [u16p, f64p, ctypes.c_size_t]
+    lib.hro_decode_bf16_vec.restype = None
+    lib.hro_round_bf16_vec.argtypes = [f64p, u16p, ctypes.c_size_t]
+    lib.hro_round_bf16_vec.restype = None
+    lib.hro_add_bf16_vec.argtypes = [u16p, u16p, u16p, ctypes.c_size_t]
+    lib.hro_add_bf16_vec.restype = None
+    lib.hro_fold_bf16.argtypes = [ctypes.POINTER(u16p), ctypes.c_int, ctypes.c_size_t, u16p]
+    lib.hro_fold_bf16.restype = None
     return lib
 
 
@@ -136,6 +145,48 @@ class Oracle:
         return out
 
 
+    # bfloat16: the same combine with bfloat16 operands and results
+    def decode_bf16(self, h) -> np.ndarray:
+        """Exact binary64 value of each bfloat16 bit pattern."""
+        h = _u16(h)
+        out = np.empty(h.shape, dtype=np.float64)
+        self.lib.hro_decode_bf16_vec(_ptr(h, ctypes.c_uint16), _ptr(out, ctypes.c_double), h.size)
+        return out
+
+    def round_bf16(self, v) -> np.ndarray:
+        """Round binary64 values to bfloat16 bit patterns, ties to even."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, dtype=np.uint16)
+        self.lib.hro_round_bf16_vec(_ptr(v, ctypes.c_double), _ptr(out, ctypes.c_uint16), v.size)
+        return out
+
+    def add_bf16(self, a, b) -> np.ndarray:
+        """Elementwise bfloat16 fl(a + b) with one rounding."""
+        a = _u16(a)
+        b = _u16(b)
+        if a.shape != b.shape:
+            raise ValueError("shape mismatch")
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.hro_add_bf16_vec(_ptr(a, ctypes.c_uint16), _ptr(b, ctypes.c_uint16),
+                                  _ptr(out, ctypes.c_uint16), a.size)
+        return out
+
+    def fold_bf16(self, xs) -> np.ndarray:
+        """Left fold of bfloat16 contributions in rank order."""
+        xs = [_u16(x) for x in xs]
+        if not xs:
+            raise ValueError("need at least one contribution")
+        n = xs[0].size
+        for x in xs:
+            if x.size != n:
+                raise ValueError("contributions differ in length")
+        out = np.empty(xs[0].shape, dtype=np.uint16)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        arr = (u16p * len(xs))(*[_ptr(x, ctypes.c_uint16) for x in xs])
+        self.lib.hro_fold_bf16(arr, len(xs), n, _ptr(out, ctypes.c_uint16))
+        return out
+
+
 _default = None
 
 
@@ -166,6 +217,35 @@ def add(a, b) -> np.ndarray:
 def fold(xs, threads: int = 1):
     """Left fold of ``xs[0..G-1]`` in rank order; see ``Oracle.fold``."""
     return _get().fold(xs, threads)
+
+
+def decode_bf16(h) -> np.ndarray:
+    """Exact binary64 value of each bfloat16 bit pattern."""
+    return _get().decode_bf16(h)
+
+
+def round_bf16(v) -> np.ndarray:
+    """Round binary64 values to bfloat16 bit patterns, ties to even."""
+    return _get().round_bf16(v)
+
+
+def add_bf16(a, b) -> np.ndarray:
+    """Elementwise bfloat16 fl(a + b) with one rounding."""
+    return _get().add_bf16(a, b)
+
+
+def fold_bf16(xs) -> np.ndarray:
+    """Left fold of bfloat16 contributions in rank order."""
+    return _get().fold_bf16(xs)
+
+
+def same_bits_bf16(a, b) -> np.ndarray:
+    """Elementwise equality of bfloat16 patterns with NaN compared by class."""
+    a = _u16(a)
+    b = _u16(b)
+    a_nan = ((a & 0x7F80) == 0x7F80) & ((a & 0x007F) != 0)
+    b_nan = ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+    return np.where(a_nan | b_nan, a_nan & b_nan, a == b)
 
 
 def same_bits(a, b) -> np.ndarray:

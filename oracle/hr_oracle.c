@@ -175,3 +175,109 @@ int hro_fold_threads(const uint16_t *const *x, int G, size_t n, uint16_t *out,
 #endif
     return used;
 }
+
+/* ------------------------------------------------------------------ bf16 --
+ *
+ * The same combine on bfloat16 operands (the SGLang pull request "[SM120]
+ * Add optional FlashInfer PCIe-IPC all-reduce for switch-free hosts" runs
+ * its reduction in bf16; section "Accuracy").  bfloat16 layout: sign bit 15,
+ * exponent field bits 14..7 (bias 127), fraction bits 6..0.  Exponent field
+ * 0 encodes zero and subnormals m * 2^-133; 255 encodes infinity (fraction
+ * 0) or NaN.
+ *
+ * Unlike binary16, the binary64 sum of two bfloat16 values is not always
+ * exact (their exponents may differ by up to 254).  One rounding to
+ * binary64 followed by one rounding to bfloat16 still equals the single
+ * correctly rounded bfloat16 sum, because 53 >= 2 * 8 + 2 (Figueroa's
+ * double-rounding condition for +, with 8-bit bfloat16 significands).  Sums
+ * whose exponents are close enough to matter in the bfloat16 subnormal range
+ * are exact in binary64, so gradual underflow is unaffected.
+ */
+
+/* Value of a bfloat16 bit pattern, exactly, as a double. */
+double hro_decode_bf16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int efield = (h >> 7) & 255;
+    int frac = h & 127;
+    double mag;
+    if (efield == 0) {
+        mag = ldexp((double)frac, -133);            /* zero or subnormal */
+    } else if (efield == 255) {
+        mag = (frac == 0) ? INFINITY : NAN;
+    } else {
+        mag = ldexp((double)(128 + frac), efield - 134); /* (1.f) * 2^(e-127) */
+    }
+    return sign ? -mag : mag;
+}
+
+/* Round a double to the nearest bfloat16, ties to even, with gradual
+ * underflow and overflow to infinity.  NaN gives the quiet NaN 0x7FC0. */
+uint16_t hro_round_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+
+    if (a < ldexp(1.0, -126)) {
+        /* subnormal range: q * 2^-133, q in [0, 128]; 128 spells the
+         * smallest normal 0x0080 */
+        double q = round_half_even(ldexp(a, 133));
+        return sign | (uint16_t)q;
+    }
+
+    /* a = f * 2^ex, f in [0.5, 1): exponent field ex + 126, significand
+     * scaled to an integer f * 2^8 in [128, 256) */
+    int ex;
+    double f = frexp(a, &ex);
+    int efield = ex + 126;
+    if (efield >= 255)
+        return sign | 0x7F80;
+    double q = round_half_even(ldexp(f, 8));
+    if (q == 256.0) {
+        q = 128.0;
+        efield += 1;
+        if (efield >= 255)
+            return sign | 0x7F80;
+    }
+    return sign | (uint16_t)(efield << 7) | (uint16_t)((int)q - 128);
+}
+
+uint16_t hro_add_bf16(uint16_t a, uint16_t b)
+{
+    return hro_round_bf16(hro_decode_bf16(a) + hro_decode_bf16(b));
+}
+
+void hro_add_bf16_vec(const uint16_t *a, const uint16_t *b, uint16_t *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = hro_add_bf16(a[i], b[i]);
+}
+
+void hro_decode_bf16_vec(const uint16_t *h, double *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = hro_decode_bf16(h[i]);
+}
+
+void hro_round_bf16_vec(const double *v, uint16_t *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = hro_round_bf16(v[i]);
+}
+
+/* Left fold of G bfloat16 contributions in rank order, one rounding per add. */
+void hro_fold_bf16(const uint16_t *const *x, int G, size_t n, uint16_t *out)
+{
+    for (size_t i = 0; i < n; ++i) {
+        uint16_t acc = x[0][i];
+        for (int g = 1; g < G; ++g)
+            acc = hro_round_bf16(hro_decode_bf16(acc) + hro_decode_bf16(x[g][i]));
+        out[i] = acc;
+    }
+}

@@ -115,6 +115,52 @@ def battery(o: oracle.Oracle) -> list:
     return failed
 
 
+MUTANTS_BF16 = {
+    "bf16_exponent_bias": ("ldexp((double)(128 + frac), efield - 134)",
+                           "ldexp((double)(128 + frac), efield - 133)"),
+    "bf16_flush_subnormals": ("mag = ldexp((double)frac, -133);", "mag = 0.0;"),
+    "bf16_fraction_width": ("double q = round_half_even(ldexp(f, 8));",
+                            "double q = round_half_even(ldexp(f, 7));"),
+    "bf16_no_overflow": ("    if (efield >= 255)\n        return sign | 0x7F80;\n    double q = round_half_even(ldexp(f, 8));",
+                         "    double q = round_half_even(ldexp(f, 8));"),
+    "bf16_right_fold": ("""        uint16_t acc = x[0][i];
+        for (int g = 1; g < G; ++g)
+            acc = hro_round_bf16(hro_decode_bf16(acc) + hro_decode_bf16(x[g][i]));""",
+                        """        uint16_t acc = x[G - 1][i];
+        for (int g = G - 2; g >= 0; --g)
+            acc = hro_round_bf16(hro_decode_bf16(x[g][i]) + hro_decode_bf16(acc));"""),
+}
+
+
+def battery_bf16(o: oracle.Oracle) -> list:
+    import torch
+    failed = []
+    allp = np.arange(65536, dtype=np.uint16)
+    is_nan = ((allp & 0x7F80) == 0x7F80) & ((allp & 0x7F) != 0)
+    ref = torch.from_numpy(allp.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = o.decode_bf16(allp)
+    if not (np.array_equal(np.isnan(got), is_nan) and
+            np.array_equal(got[~is_nan].view(np.uint64), ref[~is_nan].view(np.uint64))):
+        failed.append("decode_vs_torch")
+    if not np.array_equal(o.round_bf16(ref[~is_nan]), allp[~is_nan]):
+        failed.append("round_trip")
+    big = np.array([3.3895313892515355e38 + 2.0 ** 119, 2.0 ** 128])   # max + half ulp ties up
+    if not (o.round_bf16(big) == 0x7F80).all():
+        failed.append("overflow")
+    with open(os.path.join(GOLDEN, "worked_values_bf16.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                a, b, r = (np.array([int(t, 16)], np.uint16) for t in line.split()[:3])
+                if not oracle.same_bits_bf16(o.add_bf16(a, b), r)[0]:
+                    failed.append("worked_values")
+                    break
+    xs = [np.array([0x4380], np.uint16), np.array([0x3F80], np.uint16), np.array([0x3F80], np.uint16)]
+    if int(o.fold_bf16(xs)[0]) != 0x4380:
+        failed.append("fold_order")
+    return failed
+
+
 def _build(tmp_path, name, text):
     src = tmp_path / f"{name}.c"
     lib = tmp_path / f"lib{name}.so"
@@ -143,4 +189,20 @@ def test_mutant_is_caught(tmp_path, name):
         # only the single-threaded fold is mutated; hro_fold_threads keeps its own loop
         mutated = text.replace(old, new, 1)
     failed = battery(_build(tmp_path, name, mutated))
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_unmodified_oracle_passes_bf16_battery(tmp_path):
+    with open(SRC) as f:
+        text = f.read()
+    assert battery_bf16(_build(tmp_path, "orig_bf16", text)) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_BF16))
+def test_bf16_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS_BF16[name]
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique"
+    failed = battery_bf16(_build(tmp_path, name, text.replace(old, new)))
     assert failed, f"mutant {name} passed every pin"
