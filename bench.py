@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=32)
     p.add_argument("--quick", action="store_true", help="headline only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
-    p.add_argument("--only", default="", help="comma list of sections: probe,exchange,fold,c5")
+    p.add_argument("--only", default="", help="comma list of sections: exchange,fold,c5,bf16")
     p.add_argument("--profile-kernel", choices=("fold", "exchange", "copy"), default=None,
                    help="run one kernel --reps times and nothing else (for rocprofv3 counters)")
     p.add_argument("--reps", type=int, default=10)
@@ -456,6 +456,64 @@ def fold_workload(c: Ctx, name, xs, prefill=False):
     return res
 
 
+# ------------------------------------------------------------------ bf16
+
+def bf16_workloads(c: Ctx, link_peak):
+    """The bfloat16 variants at the prefill-sized fold and the 256 KiB
+    exchange, checked against torch's bfloat16 adds on the device."""
+    torch, hr, inputs = c.torch, c.hr, c.inputs
+
+    def dev(bits):
+        return torch.from_numpy(c.np.ascontiguousarray(bits).view(c.np.int16)).view(
+            torch.bfloat16).to(c.dev)
+
+    res = {}
+    n, G = 16_777_216, 8
+    xs = [inputs.gaussian_bf16(n, 1.0, 4, r) for r in range(G)]
+    sets = [[dev(x) for x in xs]]
+    sets += [[t.clone() for t in sets[0]] for _ in range(2)]
+    outs = [torch.empty_like(sets[0][0]) for _ in range(3)]
+    t_cold = fold_time_rotating(c, sets, outs)
+    acc = sets[0][0].clone()
+    for t in sets[0][1:]:
+        acc = acc + t
+    exact = all(torch.equal(o.view(torch.int16), acc.view(torch.int16)) for o in outs)
+    alg = (G + 1) * n * 2
+    res["fold_G8_N16777216"] = {"cold_us": round(t_cold * 1e6, 3),
+                                "cold_GBps": round(alg / t_cold / 1e9, 2),
+                                "cold_frac_hbm": round(alg / t_cold / 1e9 / HBM_PEAK_GBS, 4),
+                                "bit_exact": exact}
+    del sets, outs, acc
+
+    xb = [inputs.gaussian_bf16(131_072, 0.5, 2, r) for r in range(2)]
+    x = [dev(b) for b in xb]
+    o = [torch.empty_like(t) for t in x]
+    ref = (x[0] + x[1]).view(torch.int16)
+    ch = hr.Channel(timeout_us=5_000_000)
+    try:
+        for _ in range(20):
+            ch.allreduce(0, x[0], o[0], c.streams[0])
+            ch.allreduce(1, x[1], o[1], c.streams[1])
+        torch.cuda.synchronize()
+        steps = 500
+        graphs = [capture_calls(c, ch, r, x[r], o[r], c.streams[r], steps) for r in range(2)]
+        replay_pair(c, graphs, 10.0)
+        elapsed, _ = replay_pair(c, graphs, 10.0)
+        if ch.status() != hr.HR_OK:
+            raise RuntimeError(hr.hr_status_str(ch.status()))
+        exact = all(torch.equal(t.view(torch.int16), ref) for t in o)
+        del graphs
+        torch.cuda.synchronize()
+    finally:
+        ch.destroy()
+    t = elapsed / steps
+    alg = 3 * 131_072 * 2
+    res["exchange_2rank_256KiB_graph"] = {"us": round(t * 1e6, 3), "GBps": round(alg / t / 1e9, 2),
+                                          "frac_link": round(alg / t / 1e9 / link_peak, 4),
+                                          "bit_exact": exact}
+    return res
+
+
 # -------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(c: Ctx, tokens, gpu_out):
@@ -652,6 +710,10 @@ def main():
             log("fold G=8 N=16777216")
             cfgs["fold_G8_N16777216"] = fold_workload(c, "w4", c.inputs.workload4(), prefill=True)
 
+    if not args.quick and want("bf16"):
+        log("bf16: fold G=8 N=16777216 and two-rank exchange at 256 KiB")
+        cfgs["bf16"] = bf16_workloads(c, link_peak)
+
     cpu = None
     if not args.no_cpu:
         log("CPU oracle baseline")
@@ -683,8 +745,8 @@ def main():
                    "parallelism": "none (one GPU; two ranks as two co-resident launches)"},
         "roofline": {"bound": "host-link", "achieved": round(achieved, 3), "peak": link_peak,
                      "unit": "GB/s", "frac": round(achieved / link_peak, 4),
-                     "traffic": measured_traffic("exchange_f16"),
-                     "kernel": "hr::exchange_f16<u32x4>",
+                     "traffic": measured_traffic("exchange_k<2,true,F16>"),
+                     "kernel": "hr::exchange_k<2, true, hr::F16>",
                      "peak_source": "pinned hipMemcpyAsync probe, max(H2D, D2H) at 64 MiB, this run",
                      "link_GBps_per_dir": head["link_GBps_per_dir"]},
         "bit_exact": head["bit_exact"],
@@ -697,12 +759,12 @@ def main():
     if "fold_G8_N16777216" in cfgs:
         f4 = cfgs["fold_G8_N16777216"]
         line["roofline_hbm_fold"] = {
-            "bound": "hbm", "kernel": "hr::fold_f16_vec<8,2>", "G": 8, "N": f4["N"],
+            "bound": "hbm", "kernel": "hr::fold_vec<8, 2, hr::F16>", "G": 8, "N": f4["N"],
             "achieved": f4["cold_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": f4["cold_frac_hbm"], "protocol": "3 rotating input sets, back-to-back",
             "staggered_frac": f4["cold_staggered_frac_hbm"], "warm_frac": f4["warm_frac_hbm"],
             "single_launch_frac": f4["cold_single_frac_hbm"],
-            "traffic": measured_traffic("fold_f16_vec<8,2>"),
+            "traffic": measured_traffic("fold_vec<8,2,F16>"),
         }
     if cpu is not None:
         line["cpu_baseline"] = {

@@ -196,6 +196,19 @@ HR_API hr_status hr_reduce_f16(const void *const *inputs, int G, void *out, size
                                hr_stream_t stream);
 
 /*
+ * hr_reduce_bf16 / hr_allreduce_bf16 -- the same two operations on bfloat16
+ * values (sign, 8-bit exponent, 7-bit fraction): left fold in rank order,
+ * one bfloat16 rounding to nearest even per add, subnormals kept.  The SGLang
+ * page's reductions are bfloat16 ("Accuracy").  Arguments, layout, ownership
+ * and errors are those of the binary16 functions; a channel carries either
+ * type, but all ranks of one call must use the same one.
+ */
+HR_API hr_status hr_reduce_bf16(const void *const *inputs, int G, void *out, size_t numel,
+                                hr_stream_t stream);
+HR_API hr_status hr_allreduce_bf16(hr_channel ch, int rank, const void *in, void *out,
+                                   size_t numel, hr_stream_t stream);
+
+/*
  * hr_channel_status -- the channel's sticky asynchronous status: HR_OK, or
  * HR_ERR_TIMEOUT / HR_ERR_ABORTED once a kernel has recorded one.  Reads a
  * host-mapped word; it does not synchronise, so synchronise the rank streams

@@ -1,5 +1,7 @@
-// exchange.hip -- the FP16 all-reduce of a W-rank group through pinned
-// host slots (W = 2 is the method of the source; 3..8 extend it).
+// exchange.hip -- the FP16 (and bfloat16) all-reduce of a W-rank group
+// through pinned host slots (W = 2 is the method of the source; 3..8 extend
+// it).  The slots only carry 16-bit patterns, so one channel serves both
+// element types; the ranks of one call must use the same type.
 //
 // The method is the one the 1Cat-vLLM pull request "[Kernel] Two-rank FP16
 // all-reduce through pinned host memory for GPUs without P2P" lays out in
@@ -90,8 +92,10 @@ struct ExchArgs {
     int nactive;   // workgroups that carry values in this call
 };
 
-__device__ __forceinline__ u32x4 combine(u32x4 x0, u32x4 x1) { return add_f16x8(x0, x1); }
-__device__ __forceinline__ uint16_t combine(uint16_t x0, uint16_t x1) { return add_f16x1(x0, x1); }
+template <class E>
+__device__ __forceinline__ u32x4 combine(u32x4 x0, u32x4 x1) { return E::add8(x0, x1); }
+template <class E>
+__device__ __forceinline__ uint16_t combine(uint16_t x0, uint16_t x1) { return E::add1(x0, x1); }
 
 // Units per lane per combine batch: W loads each, at most 8 in flight.
 template <int W>
@@ -143,9 +147,10 @@ struct HostIO<uint16_t> {
 // rank whichever access path (16-byte or 2-byte) each rank takes.
 //
 // W is the group size; VEC selects the lane access unit: one 16-byte unit
-// (all buffers 16-byte aligned) or one value (2-byte aligned buffers).
-template <int W, bool VEC>
-__global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
+// (all buffers 16-byte aligned) or one value (2-byte aligned buffers); E is
+// the element type (binary16 or bfloat16).
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
     __shared__ uint32_t s_epoch;
     __shared__ uint32_t s_status;
     const int b = blockIdx.x;
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
             if (v < uhi) {
                 T acc = x[0][u];
 #pragma unroll
-                for (int q = 1; q < W; ++q) acc = combine(acc, x[q][u]);
+                for (int q = 1; q < W; ++q) acc = combine<E>(acc, x[q][u]);
                 out[v] = acc;
             }
         }
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange_f16(ExchArgs a) {
 #pragma unroll
         for (int q = 0; q < W; ++q) {
             const uint16_t xq = (q == rank) ? static_cast<const uint16_t *>(a.in)[i] : HostIO<uint16_t>::load(slot[q], i);
-            acc = (q == 0) ? xq : add_f16x1(acc, xq);
+            acc = (q == 0) ? xq : E::add1(acc, xq);
         }
         static_cast<uint16_t *>(a.out)[i] = acc;
     }
@@ -294,23 +299,24 @@ inline int active_blocks(size_t numel, int nblocks, int world) {
     return static_cast<int>(want);
 }
 
-template <int W>
+template <int W, class E>
 void launch_exchange(const ExchArgs &a, bool vec, hipStream_t s) {
     if (vec)
-        hipLaunchKernelGGL((exchange_f16<W, true>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+        hipLaunchKernelGGL((exchange_k<W, true, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((exchange_f16<W, false>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+        hipLaunchKernelGGL((exchange_k<W, false, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
 }
 
-inline void launch_exchange_w(const ExchArgs &a, bool vec, hipStream_t s) {
+template <class E>
+void launch_exchange_w(const ExchArgs &a, bool vec, hipStream_t s) {
     switch (a.world) {
-        case 2: launch_exchange<2>(a, vec, s); break;
-        case 3: launch_exchange<3>(a, vec, s); break;
-        case 4: launch_exchange<4>(a, vec, s); break;
-        case 5: launch_exchange<5>(a, vec, s); break;
-        case 6: launch_exchange<6>(a, vec, s); break;
-        case 7: launch_exchange<7>(a, vec, s); break;
-        case 8: launch_exchange<8>(a, vec, s); break;
+        case 2: launch_exchange<2, E>(a, vec, s); break;
+        case 3: launch_exchange<3, E>(a, vec, s); break;
+        case 4: launch_exchange<4, E>(a, vec, s); break;
+        case 5: launch_exchange<5, E>(a, vec, s); break;
+        case 6: launch_exchange<6, E>(a, vec, s); break;
+        case 7: launch_exchange<7, E>(a, vec, s); break;
+        case 8: launch_exchange<8, E>(a, vec, s); break;
         default: break;
     }
 }
@@ -418,8 +424,10 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     return HR_OK;
 }
 
-extern "C" HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void *in, void *out, size_t numel,
-                                             hr_stream_t stream) {
+namespace {
+
+template <class E>
+hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, size_t numel, hr_stream_t stream) {
     if (ch == nullptr || rank < 0 || rank >= ch->world_size) return HR_ERR_INVALID_ARG;
     const uint32_t sticky = __atomic_load_n(
         reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->error_off), __ATOMIC_ACQUIRE);
@@ -451,8 +459,20 @@ extern "C" HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void
     a.nblocks = ch->nblocks;
     a.nactive = active_blocks(numel, ch->nblocks, ch->world_size);
 
-    launch_exchange_w(a, aligned(in, 16) && aligned(out, 16), reinterpret_cast<hipStream_t>(stream));
+    launch_exchange_w<E>(a, aligned(in, 16) && aligned(out, 16), reinterpret_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void *in, void *out, size_t numel,
+                                             hr_stream_t stream) {
+    return allreduce_impl<F16>(ch, rank, in, out, numel, stream);
+}
+
+extern "C" HR_API hr_status hr_allreduce_bf16(hr_channel ch, int rank, const void *in, void *out, size_t numel,
+                                              hr_stream_t stream) {
+    return allreduce_impl<BF16>(ch, rank, in, out, numel, stream);
 }
 
 extern "C" HR_API hr_status hr_channel_status(hr_channel ch) {

@@ -1,4 +1,5 @@
-// fold.hip -- hr_reduce_f16: left fold of G binary16 contributions in HBM.
+// fold.hip -- hr_reduce_f16 / hr_reduce_bf16: left fold of G binary16 (or
+// bfloat16) contributions in HBM.
 //
 // R[i] = fl16(...fl16(fl16(x0[i] + x1[i]) + x2[i])... + x_{G-1}[i]), one
 // rounding per add, rank order fixed (the all-reduce's local combine; the
@@ -42,8 +43,8 @@ struct FoldShape {
     static constexpr int U = (16 / G) > 0 ? (16 / G) : 1;
 };
 
-template <int G, int U>
-__global__ __launch_bounds__(kFoldThreads) void fold_f16_vec(FoldArgs a) {
+template <int G, int U, class E>
+__global__ __launch_bounds__(kFoldThreads) void fold_vec(FoldArgs a) {
     const size_t nvec = a.nvec;
     const size_t tile = static_cast<size_t>(kFoldThreads) * U;
     const size_t step = static_cast<size_t>(gridDim.x) * tile;
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kFoldThreads) void fold_f16_vec(FoldArgs a) {
             if (v < nvec) {
                 u32x4 acc = x[0][u];
 #pragma unroll
-                for (int g = 1; g < G; ++g) acc = add_f16x8(acc, x[g][u]);
+                for (int g = 1; g < G; ++g) acc = E::add8(acc, x[g][u]);
                 __builtin_nontemporal_store(acc, out + v);
             }
         }
@@ -78,19 +79,20 @@ __global__ __launch_bounds__(kFoldThreads) void fold_f16_vec(FoldArgs a) {
         if (i < a.numel) {
             uint16_t acc = static_cast<const uint16_t *>(a.in[0])[i];
 #pragma unroll
-            for (int g = 1; g < G; ++g) acc = add_f16x1(acc, static_cast<const uint16_t *>(a.in[g])[i]);
+            for (int g = 1; g < G; ++g) acc = E::add1(acc, static_cast<const uint16_t *>(a.in[g])[i]);
             static_cast<uint16_t *>(a.out)[i] = acc;
         }
     }
 }
 
 // One value per lane, for pointers that are only 2-byte aligned.
-__global__ __launch_bounds__(kFoldThreads) void fold_f16_scalar(FoldArgs a, int G) {
+template <class E>
+__global__ __launch_bounds__(kFoldThreads) void fold_scalar(FoldArgs a, int G) {
     const size_t step = static_cast<size_t>(gridDim.x) * kFoldThreads;
     uint16_t *out = static_cast<uint16_t *>(a.out);
     for (size_t i = blockIdx.x * static_cast<size_t>(kFoldThreads) + threadIdx.x; i < a.numel; i += step) {
         uint16_t acc = static_cast<const uint16_t *>(a.in[0])[i];
-        for (int g = 1; g < G; ++g) acc = add_f16x1(acc, static_cast<const uint16_t *>(a.in[g])[i]);
+        for (int g = 1; g < G; ++g) acc = E::add1(acc, static_cast<const uint16_t *>(a.in[g])[i]);
         out[i] = acc;
     }
 }
@@ -99,7 +101,7 @@ namespace {
 
 std::atomic<int> g_cus[64];
 
-template <int G>
+template <int G, class E>
 hipError_t launch_vec(const FoldArgs &a, int cus, hipStream_t s) {
     constexpr int U = FoldShape<G>::U;
     const size_t tiles = (a.nvec + static_cast<size_t>(kFoldThreads) * U - 1) / (static_cast<size_t>(kFoldThreads) * U);
@@ -108,28 +110,29 @@ hipError_t launch_vec(const FoldArgs &a, int cus, hipStream_t s) {
     const size_t cap = static_cast<size_t>(cus) * 32;
     size_t grid = tiles < cap ? tiles : cap;
     if (grid == 0) grid = 1;  // the tail alone
-    hipLaunchKernelGGL((fold_f16_vec<G, U>), dim3(static_cast<unsigned>(grid)), dim3(kFoldThreads), 0, s, a);
+    hipLaunchKernelGGL((fold_vec<G, U, E>), dim3(static_cast<unsigned>(grid)), dim3(kFoldThreads), 0, s, a);
     return hipGetLastError();
 }
 
+template <class E>
 hipError_t launch_vec_g(int G, const FoldArgs &a, int cus, hipStream_t s) {
     switch (G) {
-        case 1: return launch_vec<1>(a, cus, s);
-        case 2: return launch_vec<2>(a, cus, s);
-        case 3: return launch_vec<3>(a, cus, s);
-        case 4: return launch_vec<4>(a, cus, s);
-        case 5: return launch_vec<5>(a, cus, s);
-        case 6: return launch_vec<6>(a, cus, s);
-        case 7: return launch_vec<7>(a, cus, s);
-        case 8: return launch_vec<8>(a, cus, s);
-        case 9: return launch_vec<9>(a, cus, s);
-        case 10: return launch_vec<10>(a, cus, s);
-        case 11: return launch_vec<11>(a, cus, s);
-        case 12: return launch_vec<12>(a, cus, s);
-        case 13: return launch_vec<13>(a, cus, s);
-        case 14: return launch_vec<14>(a, cus, s);
-        case 15: return launch_vec<15>(a, cus, s);
-        case 16: return launch_vec<16>(a, cus, s);
+        case 1: return launch_vec<1, E>(a, cus, s);
+        case 2: return launch_vec<2, E>(a, cus, s);
+        case 3: return launch_vec<3, E>(a, cus, s);
+        case 4: return launch_vec<4, E>(a, cus, s);
+        case 5: return launch_vec<5, E>(a, cus, s);
+        case 6: return launch_vec<6, E>(a, cus, s);
+        case 7: return launch_vec<7, E>(a, cus, s);
+        case 8: return launch_vec<8, E>(a, cus, s);
+        case 9: return launch_vec<9, E>(a, cus, s);
+        case 10: return launch_vec<10, E>(a, cus, s);
+        case 11: return launch_vec<11, E>(a, cus, s);
+        case 12: return launch_vec<12, E>(a, cus, s);
+        case 13: return launch_vec<13, E>(a, cus, s);
+        case 14: return launch_vec<14, E>(a, cus, s);
+        case 15: return launch_vec<15, E>(a, cus, s);
+        case 16: return launch_vec<16, E>(a, cus, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -161,8 +164,10 @@ hipError_t stream_device(hr_stream_t stream, int *device) {
 
 using namespace hr;
 
-extern "C" HR_API hr_status hr_reduce_f16(const void *const *inputs, int G, void *out, size_t numel,
-                                          hr_stream_t stream) {
+namespace {
+
+template <class E>
+hr_status reduce_impl(const void *const *inputs, int G, void *out, size_t numel, hr_stream_t stream) {
     if (G < 1 || G > HR_MAX_G) return HR_ERR_INVALID_ARG;
     if (numel == 0) return HR_OK;
     if (inputs == nullptr || out == nullptr) return HR_ERR_INVALID_ARG;
@@ -189,15 +194,27 @@ extern "C" HR_API hr_status hr_reduce_f16(const void *const *inputs, int G, void
 
     hipError_t e;
     if (vec) {
-        e = launch_vec_g(G, a, cus, s);
+        e = launch_vec_g<E>(G, a, cus, s);
     } else {
         const size_t blocks = (numel + kFoldThreads - 1) / kFoldThreads;
         const size_t cap = static_cast<size_t>(cus) * 32;
-        hipLaunchKernelGGL(fold_f16_scalar, dim3(static_cast<unsigned>(blocks < cap ? blocks : cap)),
+        hipLaunchKernelGGL(fold_scalar<E>, dim3(static_cast<unsigned>(blocks < cap ? blocks : cap)),
                            dim3(kFoldThreads), 0, s, a, G);
         e = hipGetLastError();
     }
     return e == hipSuccess ? HR_OK : HR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" HR_API hr_status hr_reduce_f16(const void *const *inputs, int G, void *out, size_t numel,
+                                          hr_stream_t stream) {
+    return reduce_impl<F16>(inputs, G, out, numel, stream);
+}
+
+extern "C" HR_API hr_status hr_reduce_bf16(const void *const *inputs, int G, void *out, size_t numel,
+                                           hr_stream_t stream) {
+    return reduce_impl<BF16>(inputs, G, out, numel, stream);
 }
 
 extern "C" HR_API const char *hr_status_str(hr_status s) {

@@ -4,6 +4,13 @@
 // lowers to one v_pk_add_f16, which adds two lanes with IEEE
 // round-to-nearest-even and keeps subnormals (the default f16 denormal mode
 // is left untouched; the library is built without fast-math).
+//
+// bfloat16 has no packed add on gfx950: a pair of __bf16 is widened to two
+// binary32 values (exact), added with v_add_f32 and narrowed by one
+// v_cvt_pk_bf16_f32 (round to nearest even).  Rounding to binary32 and then
+// to bfloat16 equals one correct rounding of the exact sum because
+// 24 >= 2 * 8 + 2; binary32 denormals are kept (default mode), so bfloat16
+// subnormals are exact.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,6 +24,7 @@
 namespace hr {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Bytes per vector unit: one 16-byte global_load/store_dwordx4 = 8 binary16.
@@ -42,6 +50,36 @@ __device__ __forceinline__ uint16_t add_f16x1(uint16_t a, uint16_t b) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(__builtin_bit_cast(_Float16, a) +
                                                               __builtin_bit_cast(_Float16, b)));
 }
+
+// bfloat16 counterparts of the three adds above.
+__device__ __forceinline__ uint32_t add_pk_bf16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(bf16x2, a) + __builtin_bit_cast(bf16x2, b));
+}
+
+__device__ __forceinline__ u32x4 add_bf16x8(u32x4 a, u32x4 b) {
+    u32x4 r;
+    r.x = add_pk_bf16(a.x, b.x);
+    r.y = add_pk_bf16(a.y, b.y);
+    r.z = add_pk_bf16(a.z, b.z);
+    r.w = add_pk_bf16(a.w, b.w);
+    return r;
+}
+
+__device__ __forceinline__ uint16_t add_bf16x1(uint16_t a, uint16_t b) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(static_cast<float>(__builtin_bit_cast(__bf16, a)) +
+                                                            static_cast<float>(__builtin_bit_cast(__bf16, b))));
+}
+
+// The element type of a combine: its 8-wide and 1-wide adds, `a` first.
+struct F16 {
+    static __device__ __forceinline__ u32x4 add8(u32x4 a, u32x4 b) { return add_f16x8(a, b); }
+    static __device__ __forceinline__ uint16_t add1(uint16_t a, uint16_t b) { return add_f16x1(a, b); }
+};
+
+struct BF16 {
+    static __device__ __forceinline__ u32x4 add8(u32x4 a, u32x4 b) { return add_bf16x8(a, b); }
+    static __device__ __forceinline__ uint16_t add1(uint16_t a, uint16_t b) { return add_bf16x1(a, b); }
+};
 
 // Compute units of a device, cached after the first query.
 hipError_t device_cu_count(int device, int *cus);

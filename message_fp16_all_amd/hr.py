@@ -35,7 +35,8 @@ HR_DEFAULT_TIMEOUT_US = 1_000_000
 # Every symbol include/hr.h declares.
 EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel_status",
            "hr_channel_abort", "hr_channel_get_info", "hr_destroy", "hr_status_str",
-           "hr_loopback_stream_create", "hr_loopback_stream_destroy")
+           "hr_loopback_stream_create", "hr_loopback_stream_destroy",
+           "hr_reduce_bf16", "hr_allreduce_bf16")
 
 
 class hr_channel_config(ctypes.Structure):
@@ -82,6 +83,8 @@ def load() -> ctypes.CDLL:
     lib.hr_create_channel.argtypes = [ctypes.POINTER(hr_channel_config), ctypes.POINTER(vp)]
     lib.hr_allreduce_f16.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
     lib.hr_reduce_f16.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.hr_allreduce_bf16.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+    lib.hr_reduce_bf16.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.hr_channel_status.argtypes = [vp]
     lib.hr_channel_abort.argtypes = [vp]
     lib.hr_channel_get_info.argtypes = [vp, ctypes.POINTER(hr_channel_info)]
@@ -126,6 +129,18 @@ def hr_reduce_f16(ptrs, G: int, out_ptr: int, numel: int, stream: int) -> int:
     return load().hr_reduce_f16(arr, G, out_ptr, numel, stream)
 
 
+def hr_allreduce_bf16(ch: int, rank: int, in_ptr: int, out_ptr: int, numel: int,
+                      stream: int) -> int:
+    """Raw call; returns the hr_status code."""
+    return load().hr_allreduce_bf16(ch, rank, in_ptr, out_ptr, numel, stream)
+
+
+def hr_reduce_bf16(ptrs, G: int, out_ptr: int, numel: int, stream: int) -> int:
+    """Raw call; ``ptrs`` is a sequence of G device addresses.  Returns hr_status."""
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    return load().hr_reduce_bf16(arr, G, out_ptr, numel, stream)
+
+
 def hr_channel_status(ch: int) -> int:
     return load().hr_channel_status(ch)
 
@@ -166,10 +181,11 @@ def _check(st: int, where: str):
         raise HrError(st, where)
 
 
-def _f16_ptr(t, name: str) -> int:
+def _f16_ptr(t, name: str, dtype=None) -> int:
     import torch
-    if t.dtype != torch.float16:
-        raise TypeError(f"{name}: expected torch.float16, got {t.dtype}")
+    want = torch.float16 if dtype is None else dtype
+    if t.dtype != want:
+        raise TypeError(f"{name}: expected {want}, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name}: expected a device tensor")
     if not t.is_contiguous():
@@ -185,15 +201,19 @@ def _stream_handle(stream) -> int:
 
 
 def reduce(tensors, out, stream=None):
-    """out = left fold of ``tensors`` (torch.float16, same numel) on ``stream``."""
+    """out = left fold of ``tensors`` (all torch.float16, or all
+    torch.bfloat16, same numel) on ``stream``."""
+    import torch
     n = out.numel()
+    bf = out.dtype == torch.bfloat16
+    dt = torch.bfloat16 if bf else torch.float16
     ptrs = []
     for i, t in enumerate(tensors):
         if t.numel() != n:
             raise ValueError(f"tensors[{i}] has {t.numel()} values, out has {n}")
-        ptrs.append(_f16_ptr(t, f"tensors[{i}]"))
-    _check(hr_reduce_f16(ptrs, len(ptrs), _f16_ptr(out, "out"), n, _stream_handle(stream)),
-           "hr_reduce_f16")
+        ptrs.append(_f16_ptr(t, f"tensors[{i}]", dt))
+    fn, name = (hr_reduce_bf16, "hr_reduce_bf16") if bf else (hr_reduce_f16, "hr_reduce_f16")
+    _check(fn(ptrs, len(ptrs), _f16_ptr(out, "out", dt), n, _stream_handle(stream)), name)
     return out
 
 
@@ -207,11 +227,16 @@ class Channel:
         self.handle = hr_create_channel(device, world_size, max_numel, num_blocks, timeout_us)
 
     def allreduce(self, rank: int, inp, out, stream=None):
+        """One rank's call; torch.float16 or torch.bfloat16 tensors."""
+        import torch
         n = inp.numel()
         if out.numel() != n:
             raise ValueError("in and out differ in numel")
-        _check(hr_allreduce_f16(self.handle, rank, _f16_ptr(inp, "in"), _f16_ptr(out, "out"), n,
-                                _stream_handle(stream)), "hr_allreduce_f16")
+        bf = inp.dtype == torch.bfloat16
+        dt = torch.bfloat16 if bf else torch.float16
+        fn, name = (hr_allreduce_bf16, "hr_allreduce_bf16") if bf else (hr_allreduce_f16, "hr_allreduce_f16")
+        _check(fn(self.handle, rank, _f16_ptr(inp, "in", dt), _f16_ptr(out, "out", dt), n,
+                  _stream_handle(stream)), name)
         return out
 
     def status(self) -> int:

@@ -32,6 +32,10 @@ no data, so seeded Gaussians of those shapes are used:
 ``edge_pairs`` adds every ordered pair of 17 special values (signed zeros,
 subnormal extremes, the smallest normal, one, 2048, the largest finite, the
 infinities and a quiet NaN) so that every special meets every other.
+
+bfloat16 contributions (``gaussian_bf16``, ``edge_pairs_bf16``) take the top
+16 bits of the same binary32 draws: a bfloat16 sample of the same
+distribution, obtained by truncation so that this module does no rounding.
 """
 from __future__ import annotations
 
@@ -139,6 +143,35 @@ def workload6(world: int, tokens: int, call: int = 0):
     """`world` contributions of 4096 * tokens values for a W-rank exchange."""
     n = HIDDEN_DECODE * tokens
     return [gaussian(n, WORKLOADS[6]["sigma"], 6, r, call) for r in range(world)]
+
+
+EDGE_VALUES_BF16 = np.array([
+    0x0000, 0x8000,          # +0, -0
+    0x0001, 0x8001,          # smallest subnormals
+    0x007F, 0x807F,          # largest subnormals
+    0x0080, 0x8080,          # smallest normals
+    0x3F80, 0xBF80,          # +-1
+    0x4380, 0xC380,          # +-256
+    0x7F7F, 0xFF7F,          # +-largest finite
+    0x7F80, 0xFF80,          # +-inf
+    0x7FC0,                  # quiet NaN
+], dtype=np.uint16)
+
+
+def gaussian_bf16(n: int, sigma: float, workload: int, rank: int, call: int = 0) -> np.ndarray:
+    """n bfloat16 patterns: the top halves of N(0, sigma^2) binary32 draws."""
+    g = rng(workload, rank, call)
+    x = g.standard_normal(n, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def edge_pairs_bf16():
+    """All 289 ordered pairs of EDGE_VALUES_BF16 as two contributions."""
+    a = np.repeat(EDGE_VALUES_BF16, EDGE_VALUES_BF16.size)
+    b = np.tile(EDGE_VALUES_BF16, EDGE_VALUES_BF16.size)
+    return [a.copy(), b.copy()]
 
 
 def edge_pairs():
