@@ -258,6 +258,50 @@ HR_API hr_status hr_loopback_stream_create(int device, hr_stream_t *out);
  * hr_loopback_stream_create (after its work has finished).  NULL is a no-op. */
 HR_API hr_status hr_loopback_stream_destroy(hr_stream_t stream);
 
+/*
+ * Admission: which reductions take the host-slot all-reduce.
+ *
+ * The 1Cat-vLLM page admits FP16 payloads of two-rank groups without peer
+ * access up to 256 KiB, behind an on/off switch, and leaves everything else
+ * on the caller's existing collective ("Purpose", "Path coverage").  The
+ * SGLang page sizes its bound for decode: rows = max batch x tokens per
+ * request per step, times hidden ("Modifications").  hr_admit applies that
+ * policy (widened to bfloat16 and larger groups only when asked) and names
+ * the first reason it declines, so a decline is never silent.  Pure host
+ * logic: no device is touched.
+ */
+typedef enum {
+    HR_ROUTE_HOST = 0,           /* take hr_allreduce_f16 / _bf16 */
+    HR_DECLINE_DISABLED = 1,     /* policy switched off */
+    HR_DECLINE_DTYPE = 2,        /* not binary16 (or bfloat16 when allowed) */
+    HR_DECLINE_WORLD_SIZE = 3,   /* group size outside 2..max_world */
+    HR_DECLINE_PEER_ACCESS = 4,  /* the GPUs reach each other directly */
+    HR_DECLINE_TOO_LARGE = 5     /* payload above the cap */
+} hr_route;
+
+typedef enum { HR_DTYPE_F16 = 0, HR_DTYPE_BF16 = 1, HR_DTYPE_OTHER = 2 } hr_dtype;
+
+typedef struct {
+    int enabled;       /* 0 declines everything (HR_DECLINE_DISABLED)          */
+    size_t max_bytes;  /* payload cap per rank; 0 = 256 KiB                    */
+    int allow_bf16;    /* nonzero admits bfloat16 as well as binary16          */
+    int max_world;     /* largest group admitted; 0 = 2 (the two-rank method)  */
+} hr_admit_policy;
+
+/* Route for one reduction of `numel` values of `dtype` in a group of
+ * `world_size` ranks; `peer_access` nonzero when the GPUs can reach each
+ * other directly.  A NULL policy is the page's default: enabled, FP16 only,
+ * two ranks, 256 KiB. */
+HR_API hr_route hr_admit(const hr_admit_policy *policy, hr_dtype dtype, int world_size,
+                         int peer_access, size_t numel);
+
+/* Static name of a route. */
+HR_API const char *hr_route_str(hr_route r);
+
+/* Decode-sized bound in values: max_batch x tokens_per_request (0 counts as
+ * 1) x hidden -- e.g. 64 x 1 x 6144 = 393216, the SGLang page's default. */
+HR_API size_t hr_decode_numel(size_t max_batch, size_t tokens_per_request, size_t hidden);
+
 /* Static, human-readable name of a status code. */
 HR_API const char *hr_status_str(hr_status s);
 

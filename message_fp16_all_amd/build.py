@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhr.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("fold.hip", "exchange.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fold.hip", "exchange.hip", "admit.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -36,7 +36,17 @@ HR_DEFAULT_TIMEOUT_US = 1_000_000
 EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel_status",
            "hr_channel_abort", "hr_channel_get_info", "hr_destroy", "hr_status_str",
            "hr_loopback_stream_create", "hr_loopback_stream_destroy",
-           "hr_reduce_bf16", "hr_allreduce_bf16")
+           "hr_reduce_bf16", "hr_allreduce_bf16", "hr_admit", "hr_route_str", "hr_decode_numel")
+
+HR_ROUTE_HOST = 0
+HR_DECLINE_DISABLED = 1
+HR_DECLINE_DTYPE = 2
+HR_DECLINE_WORLD_SIZE = 3
+HR_DECLINE_PEER_ACCESS = 4
+HR_DECLINE_TOO_LARGE = 5
+HR_DTYPE_F16 = 0
+HR_DTYPE_BF16 = 1
+HR_DTYPE_OTHER = 2
 
 
 class hr_channel_config(ctypes.Structure):
@@ -45,6 +55,13 @@ class hr_channel_config(ctypes.Structure):
                 ("max_numel", ctypes.c_size_t),
                 ("num_blocks", ctypes.c_int),
                 ("timeout_us", ctypes.c_uint32)]
+
+
+class hr_admit_policy(ctypes.Structure):
+    _fields_ = [("enabled", ctypes.c_int),
+                ("max_bytes", ctypes.c_size_t),
+                ("allow_bf16", ctypes.c_int),
+                ("max_world", ctypes.c_int)]
 
 
 class hr_channel_info(ctypes.Structure):
@@ -93,8 +110,14 @@ def load() -> ctypes.CDLL:
     lib.hr_loopback_stream_destroy.argtypes = [vp]
     lib.hr_status_str.argtypes = [ctypes.c_int]
     lib.hr_status_str.restype = ctypes.c_char_p
+    lib.hr_admit.argtypes = [ctypes.POINTER(hr_admit_policy), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_size_t]
+    lib.hr_route_str.argtypes = [ctypes.c_int]
+    lib.hr_route_str.restype = ctypes.c_char_p
+    lib.hr_decode_numel.argtypes = [ctypes.c_size_t, ctypes.c_size_t, ctypes.c_size_t]
+    lib.hr_decode_numel.restype = ctypes.c_size_t
     for name in EXPORTS:
-        if name != "hr_status_str":
+        if name not in ("hr_status_str", "hr_route_str", "hr_decode_numel"):
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -172,6 +195,20 @@ def hr_loopback_stream_create(device: int = 0) -> int:
 
 def hr_loopback_stream_destroy(stream: int) -> int:
     return load().hr_loopback_stream_destroy(stream)
+
+
+def hr_admit(policy, dtype: int, world_size: int, peer_access: bool, numel: int) -> int:
+    """Route code for one reduction; ``policy`` is an hr_admit_policy or None."""
+    ref = ctypes.byref(policy) if policy is not None else None
+    return load().hr_admit(ref, dtype, world_size, int(bool(peer_access)), numel)
+
+
+def hr_route_str(route: int) -> str:
+    return load().hr_route_str(int(route)).decode()
+
+
+def hr_decode_numel(max_batch: int, tokens_per_request: int, hidden: int) -> int:
+    return load().hr_decode_numel(max_batch, tokens_per_request, hidden)
 
 
 # ----------------------------------------------------- torch marshalling
