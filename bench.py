@@ -250,7 +250,7 @@ def eager_calls(c: Ctx, ch, x, o, streams, calls):
 
 
 def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=200, gate_ms=None,
-                      world=2):
+                      world=2, algorithm=0):
     torch, hr, inputs = c.torch, c.hr, c.inputs
     xb = inputs.workload2(tokens) if world == 2 else inputs.workload6(world, tokens)
     n = xb[0].size
@@ -258,7 +258,8 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
     x = [c.to_dev(b) for b in xb]
     o = [torch.empty_like(t) for t in x]
     ref = torch_fold(c, xb)
-    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=5_000_000, world_size=world)
+    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=5_000_000, world_size=world,
+                    algorithm=algorithm)
     try:
         for _ in range(warmup):
             for r in range(world):
@@ -284,10 +285,17 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
         ch.destroy()
     t_graph = elapsed / steps
     alg = (world + 1) * n * 2
-    d2h = world * n * 2                 # each rank publishes its slice once
-    h2d = world * (world - 1) * n * 2   # each rank reads every peer's slice
+    two = algorithm == hr.HR_ALGO_TWO_SHOT or (algorithm == hr.HR_ALGO_AUTO and world >= 3
+                                                and n >= 32768)
+    if two:
+        d2h = world * n * 2 + n * 2                 # contributions + folded shards
+        h2d = 2 * (world - 1) * n * 2               # peers' shard parts + folded shards
+    else:
+        d2h = world * n * 2                 # each rank publishes its slice once
+        h2d = world * (world - 1) * n * 2   # each rank reads every peer's slice
     return {
-        "world": world, "tokens": tokens, "N": n, "bytes_per_call": alg,
+        "world": world, "algorithm": "two-shot" if two else "one-shot",
+        "tokens": tokens, "N": n, "bytes_per_call": alg,
         "graph_us": round(t_graph * 1e6, 3), "graph_GBps": round(alg / t_graph / 1e9, 2),
         "graph_frac_link": round(alg / t_graph / 1e9 / link_peak, 4),
         "link_GBps_per_dir": round(max(d2h, h2d) / t_graph / 1e9, 2),
@@ -693,11 +701,13 @@ def main():
             rows = []
             for w in (4, 8):
                 for t in (1, 8, 32):
-                    log(f"exchange world={w} tokens={t}")
-                    r = exchange_workload(c, t, 300, 20, link_peak, eager_calls_n=50, world=w)
-                    r.pop("_elapsed_s")
-                    r.pop("_out")
-                    rows.append(r)
+                    for algo in (c.hr.HR_ALGO_ONE_SHOT, c.hr.HR_ALGO_TWO_SHOT):
+                        log(f"exchange world={w} tokens={t} algorithm={algo}")
+                        r = exchange_workload(c, t, 300, 20, link_peak, eager_calls_n=50, world=w,
+                                              algorithm=algo)
+                        r.pop("_elapsed_s")
+                        r.pop("_out")
+                        rows.append(r)
             cfgs["exchange_world_host_slots"] = rows
         if want("c5"):
             log("exchange graph of 1000 fresh calls, N=10240")

@@ -95,6 +95,13 @@ typedef enum {
 /* Default watchdog for one wait on the peer, in microseconds. */
 #define HR_DEFAULT_TIMEOUT_US 1000000u
 
+/* Exchange algorithm of a channel (both produce the same bits). */
+#define HR_ALGO_AUTO 0      /* one-shot for two ranks and small payloads,
+                               two-shot for 3+ ranks from 32768 values    */
+#define HR_ALGO_ONE_SHOT 1  /* every rank reads every peer's contribution */
+#define HR_ALGO_TWO_SHOT 2  /* shard owners fold, then everyone gathers;
+                               needs num_blocks >= world_size             */
+
 typedef struct {
     int device;           /* HIP device ordinal the channel's kernels run on  */
     int world_size;       /* ranks W in the group, 2..HR_MAX_WORLD; 2 is the
@@ -107,6 +114,7 @@ typedef struct {
                              GPU, so the value is clamped to the device's
                              compute units / world_size.                       */
     uint32_t timeout_us;  /* watchdog per wait; 0 = HR_DEFAULT_TIMEOUT_US      */
+    int algorithm;        /* HR_ALGO_*; 0 = automatic                         */
 } hr_channel_config;
 
 /* Read-only description of a channel, for diagnostics and tests. */
@@ -126,6 +134,11 @@ typedef struct {
     size_t flag_stride;           /* uint32 words between consecutive flags   */
     volatile uint32_t *host_error; /* sticky asynchronous status word         */
     volatile uint32_t *host_abort; /* nonzero = cancel waits                  */
+    int algorithm;                /* HR_ALGO_* the channel was created with  */
+    void *host_reduced;           /* two-shot reduced-shard slots
+                                     [2 parity][slot_stride] binary16         */
+    volatile uint32_t *host_flags2; /* two-shot reduced-shard flags, laid out
+                                     like host_flags                          */
 } hr_channel_info;
 
 /*
@@ -149,6 +162,11 @@ HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out
 
 /*
  * hr_allreduce_f16 -- one all-reduce call of rank `rank` (0..world_size-1).
+ *
+ * One-shot algorithm (below); the two-shot (HR_ALGO_TWO_SHOT, or automatic
+ * for larger groups and payloads) instead has each shard's owner fold that
+ * shard in rank order and publish it, and every rank gather the others'
+ * folded shards: less host-link traffic for W > 2, the same bits.
  *
  * Enqueues exactly one kernel on `stream`.  Its workgroups each own one
  * contiguous slice of the numel values: they copy the slice of `in` into this

@@ -80,7 +80,9 @@ struct ExchArgs {
     size_t numel;
     uint16_t *slots;          // device view of the host slot region
     size_t stride;            // values per slot
-    uint32_t *flags;          // device view of the host flags
+    uint32_t *flags;          // device view of the host flags (publish)
+    uint32_t *flags2;         // device view of the host flags (reduced shard, two-shot)
+    uint16_t *reduced;        // device view of the reduced-shard slots [2][stride] (two-shot)
     uint32_t *epochs;         // this rank's counters (HBM)
     uint32_t *dev_error;      // HBM
     uint32_t *host_error;     // device view of the host error word
@@ -140,6 +142,59 @@ struct HostIO<uint16_t> {
     }
 };
 
+// Wait, in the first wave, until flag[q][b] >= e for every rank q whose bit
+// is set in `mask` (one lane per rank, wrap-safe compare), or the abort word
+// is set, or the watchdog expires.  Returns 0, HR_ERR_ABORTED or
+// HR_ERR_TIMEOUT, the same in every lane of the wave; lane 0 records an
+// error in both error words.
+__device__ __forceinline__ uint32_t wait_flags(const ExchArgs &a, const uint32_t *flag_base, int b, uint32_t e,
+                                               unsigned mask) {
+    const int lane = threadIdx.x;
+    const bool polls = lane < kMaxWorld && ((mask >> lane) & 1u);
+    const uint32_t *pf = flag_base + (static_cast<size_t>(polls ? lane : 0) * a.nblocks + b) * kFlagStride;
+    bool done = !polls;
+    uint32_t status = 0;
+    const long long t0 = wall_clock64();
+    for (;;) {
+        if (!done) {
+            const uint32_t f = __hip_atomic_load(pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            done = static_cast<int32_t>(f - e) >= 0;
+        }
+        if (__all(done)) break;
+        uint32_t ab = 0;
+        if (lane == 0) ab = __hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (__shfl(ab, 0) != 0) {
+            status = HR_ERR_ABORTED;
+            break;
+        }
+        if (static_cast<uint64_t>(wall_clock64() - t0) > a.timeout_ticks) {
+            status = HR_ERR_TIMEOUT;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0 && status != 0) {
+        __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.host_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    return status;
+}
+
+// Advance this workgroup's call counter (every launched workgroup does, so a
+// rank's workgroups agree on the slot parity); returns the call number e, or
+// 0 when the channel already holds an error.
+__device__ __forceinline__ uint32_t next_call(const ExchArgs &a, int b) {
+    __shared__ uint32_t s_epoch;
+    if (threadIdx.x == 0) {
+        const uint32_t err = __hip_atomic_load(a.dev_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t e = __hip_atomic_load(&a.epochs[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        if (err == 0) __hip_atomic_store(&a.epochs[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_epoch = err == 0 ? e : 0u;
+    }
+    __syncthreads();
+    return s_epoch;
+}
+
 // Workgroup b of an active set of `nact` owns the 8-value units
 // [nvec*b/nact, nvec*(b+1)/nact) of the call, nvec = numel / 8, and the last
 // active workgroup also owns the numel % 8 trailing values.  The split
@@ -151,23 +206,12 @@ struct HostIO<uint16_t> {
 // the element type (binary16 or bfloat16).
 template <int W, bool VEC, class E>
 __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
-    __shared__ uint32_t s_epoch;
     __shared__ uint32_t s_status;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
 
-    // Every launched workgroup advances its call counter, active or not, so
-    // all workgroups of a rank agree on the call's slot parity.
-    if (tid == 0) {
-        const uint32_t err = __hip_atomic_load(a.dev_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t e = __hip_atomic_load(&a.epochs[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        if (err == 0) __hip_atomic_store(&a.epochs[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_epoch = e;
-        s_status = err;
-    }
-    __syncthreads();
-    if (s_status != 0 || b >= a.nactive) return;
-    const uint32_t e = s_epoch;
+    const uint32_t e = next_call(a, b);
+    if (e == 0 || b >= a.nactive) return;
     const int parity = static_cast<int>(e & 1u);
     const int rank = a.rank;
 
@@ -214,36 +258,8 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
 
     // 3. the first wave waits for every peer's flag, one lane per peer
     if (tid < 64) {
-        const bool polls = tid < W && tid != rank;
-        const uint32_t *pf = a.flags + (static_cast<size_t>(polls ? tid : 0) * a.nblocks + b) * kFlagStride;
-        bool done = !polls;
-        uint32_t status = 0;
-        const long long t0 = wall_clock64();
-        for (;;) {
-            if (!done) {
-                const uint32_t f = __hip_atomic_load(pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                done = static_cast<int32_t>(f - e) >= 0;
-            }
-            if (__all(done)) break;
-            uint32_t ab = 0;
-            if (tid == 0) ab = __hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            if (__shfl(ab, 0) != 0) {
-                status = HR_ERR_ABORTED;
-                break;
-            }
-            if (static_cast<uint64_t>(wall_clock64() - t0) > a.timeout_ticks) {
-                status = HR_ERR_TIMEOUT;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        if (tid == 0) {
-            if (status != 0) {
-                __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.host_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            }
-            s_status = status;
-        }
+        const uint32_t st = wait_flags(a, a.flags, b, e, ((1u << W) - 1u) & ~(1u << rank));
+        if (tid == 0) s_status = st;
     }
     // the barrier orders every lane's slot loads after the flags the first
     // wave saw; the loads themselves read host memory, not a cached copy
@@ -285,6 +301,165 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
     }
 }
 
+// Two-shot variant for larger payloads and groups: the active workgroups
+// form W groups of m; group s covers shard s (the 8-value units
+// [nvec*s/W, nvec*(s+1)/W), split into m contiguous sub-slices), so
+// workgroup b covers the same values on every rank.
+//   A. every workgroup publishes its own values of its sub-slice to
+//      slot[e & 1][rank] and raises flag[rank][b] = e;
+//   B. the workgroups of group `rank` wait for flag[q][b] of every peer q,
+//      fold the sub-slice left in rank order (own values from `in`), store
+//      the result to `out` and to the reduced slot red[e & 1], and raise
+//      flag2[rank][b] = e;
+//   C. the workgroups of every other group s wait for flag2[s][b] (rank
+//      s's fold of the same sub-slice) and copy it from red[e & 1] to `out`.
+// Every value is folded once, by its shard's owner, in the same order as the
+// one-shot fold, so both algorithms produce the same bits.  Host-link
+// traffic per rank: (1 + 1/W) N values written, 2 (W-1)/W N read, against N
+// and (W-1) N for the one-shot.  Parity safety: in call e + 1 the owner
+// workgroups of a rank waited for every peer's publish flag of call e + 1,
+// so every peer had finished call e, including its reads of slot and
+// reduced-slot parity e & 1, before the rank starts call e + 2.
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
+    __shared__ uint32_t s_status;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+
+    const uint32_t e = next_call(a, b);
+    if (e == 0 || b >= a.nactive) return;
+    const int parity = static_cast<int>(e & 1u);
+    const int rank = a.rank;
+    const int m = a.nactive / W;               // workgroups per shard
+    const int shard = b / m, j = b % m;
+
+    const size_t nvec = a.numel / kVecElems;
+    const size_t sh_lo = nvec * static_cast<size_t>(shard) / W;
+    const size_t sh_hi = nvec * static_cast<size_t>(shard + 1) / W;
+    const size_t lo = sh_lo + (sh_hi - sh_lo) * static_cast<size_t>(j) / static_cast<size_t>(m);
+    const size_t hi = sh_lo + (sh_hi - sh_lo) * static_cast<size_t>(j + 1) / static_cast<size_t>(m);
+    const bool last = (b == a.nactive - 1);    // shard W-1, last sub-slice: owns the tail
+    const size_t tail0 = nvec * kVecElems;
+
+    typedef typename std::conditional<VEC, u32x4, uint16_t>::type T;
+    constexpr size_t per = VEC ? kVecElems : 1;
+    const size_t ulo = lo * (kVecElems / per), uhi = hi * (kVecElems / per);
+    const T *in = static_cast<const T *>(a.in);
+    T *out = static_cast<T *>(a.out);
+    __amdgpu_buffer_rsrc_t slot[W];
+#pragma unroll
+    for (int q = 0; q < W; ++q)
+        slot[q] = slot_rsrc(a.slots + static_cast<size_t>(W * parity + q) * a.stride, a.stride);
+    const __amdgpu_buffer_rsrc_t red = slot_rsrc(a.reduced + static_cast<size_t>(parity) * a.stride, a.stride);
+
+    // A. publish
+    for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
+        T x[kExchUnroll];
+#pragma unroll
+        for (int u = 0; u < kExchUnroll; ++u) {
+            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+            if (v < uhi) x[u] = in[v];
+        }
+#pragma unroll
+        for (int u = 0; u < kExchUnroll; ++u) {
+            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+            if (v < uhi) HostIO<T>::store(slot[rank], v, x[u]);
+        }
+    }
+    if (last && tail0 + tid < a.numel)
+        HostIO<uint16_t>::store(slot[rank], tail0 + tid, static_cast<const uint16_t *>(a.in)[tail0 + tid]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_store(a.flags + (static_cast<size_t>(rank) * a.nblocks + b) * kFlagStride, e,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+
+    if (shard == rank) {
+        // B. fold this rank's shard
+        if (tid < 64) {
+            const uint32_t st = wait_flags(a, a.flags, b, e, ((1u << W) - 1u) & ~(1u << rank));
+            if (tid == 0) s_status = st;
+        }
+        __syncthreads();
+        if (s_status != 0) return;
+        constexpr int UC = CombineShape<W>::U;
+        for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * UC) {
+            T x[W][UC];
+#pragma unroll
+            for (int u = 0; u < UC; ++u) {
+                const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+                if (v < uhi) {
+#pragma unroll
+                    for (int q = 0; q < W; ++q) x[q][u] = (q == rank) ? in[v] : HostIO<T>::load(slot[q], v);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UC; ++u) {
+                const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+                if (v < uhi) {
+                    T acc = x[0][u];
+#pragma unroll
+                    for (int q = 1; q < W; ++q) acc = combine<E>(acc, x[q][u]);
+                    out[v] = acc;
+                    HostIO<T>::store(red, v, acc);
+                }
+            }
+        }
+        if (last && tail0 + tid < a.numel) {
+            const size_t i = tail0 + tid;
+            uint16_t acc = 0;
+#pragma unroll
+            for (int q = 0; q < W; ++q) {
+                const uint16_t xq =
+                    (q == rank) ? static_cast<const uint16_t *>(a.in)[i] : HostIO<uint16_t>::load(slot[q], i);
+                acc = (q == 0) ? xq : E::add1(acc, xq);
+            }
+            static_cast<uint16_t *>(a.out)[i] = acc;
+            HostIO<uint16_t>::store(red, i, acc);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(a.flags2 + (static_cast<size_t>(rank) * a.nblocks + b) * kFlagStride, e,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    } else {
+        // C. gather shard `shard` from its owner
+        if (tid < 64) {
+            const uint32_t st = wait_flags(a, a.flags2, b, e, 1u << shard);
+            if (tid == 0) s_status = st;
+        }
+        __syncthreads();
+        if (s_status != 0) return;
+        for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
+            T x[kExchUnroll];
+#pragma unroll
+            for (int u = 0; u < kExchUnroll; ++u) {
+                const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+                if (v < uhi) x[u] = HostIO<T>::load(red, v);
+            }
+#pragma unroll
+            for (int u = 0; u < kExchUnroll; ++u) {
+                const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+                if (v < uhi) out[v] = x[u];
+            }
+        }
+        if (last && tail0 + tid < a.numel)
+            static_cast<uint16_t *>(a.out)[tail0 + tid] = HostIO<uint16_t>::load(red, tail0 + tid);
+    }
+}
+
+// Active workgroups of a two-shot call: W groups of m, m about one 16-byte
+// unit per lane of the shard, at least 1, at most nblocks / W.
+inline int active_blocks2(size_t numel, int nblocks, int world) {
+    const size_t nvec = numel / kVecElems;
+    const size_t per_shard = (nvec + world - 1) / world;
+    size_t m = (per_shard + kExchThreads - 1) / kExchThreads;
+    if (m < 1) m = 1;
+    const size_t mmax = static_cast<size_t>(nblocks / world);
+    if (m > mmax) m = mmax;
+    return static_cast<int>(m) * world;
+}
+
 // Active workgroups for a call of numel values: about one 16-byte unit per
 // lane, at least 16 / W (so small calls still spread their flag traffic over
 // a few workgroups, while large groups, whose every workgroup polls W - 1
@@ -299,8 +474,29 @@ inline int active_blocks(size_t numel, int nblocks, int world) {
     return static_cast<int>(want);
 }
 
+// Which algorithm a call takes: a function of the channel and numel only,
+// so every rank of a call takes the same one.  Automatic choice: the
+// one-shot for two ranks (the source's method) and for small payloads,
+// whose latency the second handshake would double; the two-shot for
+// groups of three or more above kTwoShotMinNumel values.
+constexpr size_t kTwoShotMinNumel = 32768;
+
+inline bool use_two_shot(int algorithm, size_t numel, int world, int nblocks) {
+    if (nblocks < world) return false;
+    if (algorithm == HR_ALGO_TWO_SHOT) return true;
+    if (algorithm == HR_ALGO_ONE_SHOT) return false;
+    return world >= 3 && numel >= kTwoShotMinNumel;
+}
+
 template <int W, class E>
-void launch_exchange(const ExchArgs &a, bool vec, hipStream_t s) {
+void launch_exchange(const ExchArgs &a, bool vec, bool two_shot, hipStream_t s) {
+    if (two_shot) {
+        if (vec)
+            hipLaunchKernelGGL((exchange2_k<W, true, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((exchange2_k<W, false, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+        return;
+    }
     if (vec)
         hipLaunchKernelGGL((exchange_k<W, true, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
     else
@@ -308,15 +504,15 @@ void launch_exchange(const ExchArgs &a, bool vec, hipStream_t s) {
 }
 
 template <class E>
-void launch_exchange_w(const ExchArgs &a, bool vec, hipStream_t s) {
+void launch_exchange_w(const ExchArgs &a, bool vec, bool two_shot, hipStream_t s) {
     switch (a.world) {
-        case 2: launch_exchange<2, E>(a, vec, s); break;
-        case 3: launch_exchange<3, E>(a, vec, s); break;
-        case 4: launch_exchange<4, E>(a, vec, s); break;
-        case 5: launch_exchange<5, E>(a, vec, s); break;
-        case 6: launch_exchange<6, E>(a, vec, s); break;
-        case 7: launch_exchange<7, E>(a, vec, s); break;
-        case 8: launch_exchange<8, E>(a, vec, s); break;
+        case 2: launch_exchange<2, E>(a, vec, two_shot, s); break;
+        case 3: launch_exchange<3, E>(a, vec, two_shot, s); break;
+        case 4: launch_exchange<4, E>(a, vec, two_shot, s); break;
+        case 5: launch_exchange<5, E>(a, vec, two_shot, s); break;
+        case 6: launch_exchange<6, E>(a, vec, two_shot, s); break;
+        case 7: launch_exchange<7, E>(a, vec, two_shot, s); break;
+        case 8: launch_exchange<8, E>(a, vec, two_shot, s); break;
         default: break;
     }
 }
@@ -335,7 +531,8 @@ struct hr_channel_s {
     uint64_t timeout_ticks;
     void *host_base;           // hipHostMalloc'ed region (host address)
     unsigned char *host_dev;   // the same region as seen by the device
-    size_t flags_off, error_off, abort_off, host_bytes;
+    int algorithm;             // HR_ALGO_*
+    size_t flags_off, flags2_off, reduced_off, error_off, abort_off, host_bytes;
     uint32_t *dev_words;       // hipMalloc: epochs[world * nblocks] then the error word
 };
 
@@ -367,6 +564,7 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     if (cfg == nullptr || out == nullptr) return HR_ERR_INVALID_ARG;
     if (cfg->world_size < 2 || cfg->world_size > kMaxWorld) return HR_ERR_UNSUPPORTED;
     if (cfg->device < 0 || cfg->num_blocks < 0) return HR_ERR_INVALID_ARG;
+    if (cfg->algorithm < HR_ALGO_AUTO || cfg->algorithm > HR_ALGO_TWO_SHOT) return HR_ERR_INVALID_ARG;
     const size_t max_numel = cfg->max_numel ? cfg->max_numel : HR_DEFAULT_MAX_NUMEL;
     // A slot is addressed by a buffer descriptor whose byte count and
     // offsets are 32-bit: keep one slot at or below 1 GiB.
@@ -397,13 +595,21 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     int nb = cfg->num_blocks ? cfg->num_blocks : cus / world;
     if (nb > cus / world) nb = cus / world;
     if (nb < 1) nb = 1;
+    if (cfg->algorithm == HR_ALGO_TWO_SHOT && nb < world) {
+        delete ch;
+        return HR_ERR_INVALID_ARG;  // the two-shot needs a workgroup per shard
+    }
     ch->nblocks = nb;
+    ch->algorithm = cfg->algorithm;
     ch->timeout_us = timeout_us;
     ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
 
     const size_t slot_bytes = 2 * static_cast<size_t>(world) * ch->stride * sizeof(uint16_t);
-    ch->flags_off = round_up(slot_bytes, kLine);
-    ch->error_off = ch->flags_off + static_cast<size_t>(world) * static_cast<size_t>(nb) * kLine;
+    const size_t flag_bytes = static_cast<size_t>(world) * static_cast<size_t>(nb) * kLine;
+    ch->reduced_off = round_up(slot_bytes, kLine);
+    ch->flags_off = ch->reduced_off + 2 * ch->stride * sizeof(uint16_t);
+    ch->flags2_off = ch->flags_off + flag_bytes;
+    ch->error_off = ch->flags2_off + flag_bytes;
     ch->abort_off = ch->error_off + kLine;
     ch->host_bytes = ch->abort_off + kLine;
 
@@ -449,6 +655,8 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
     a.slots = reinterpret_cast<uint16_t *>(ch->host_dev);
     a.stride = ch->stride;
     a.flags = reinterpret_cast<uint32_t *>(ch->host_dev + ch->flags_off);
+    a.flags2 = reinterpret_cast<uint32_t *>(ch->host_dev + ch->flags2_off);
+    a.reduced = reinterpret_cast<uint16_t *>(ch->host_dev + ch->reduced_off);
     a.epochs = ch->dev_words + static_cast<size_t>(rank) * ch->nblocks;
     a.dev_error = ch->dev_words + static_cast<size_t>(ch->world_size) * ch->nblocks;
     a.host_error = reinterpret_cast<uint32_t *>(ch->host_dev + ch->error_off);
@@ -457,9 +665,11 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
     a.rank = rank;
     a.world = ch->world_size;
     a.nblocks = ch->nblocks;
-    a.nactive = active_blocks(numel, ch->nblocks, ch->world_size);
+    const bool two_shot = use_two_shot(ch->algorithm, numel, ch->world_size, ch->nblocks);
+    a.nactive = two_shot ? active_blocks2(numel, ch->nblocks, ch->world_size)
+                         : active_blocks(numel, ch->nblocks, ch->world_size);
 
-    launch_exchange_w<E>(a, aligned(in, 16) && aligned(out, 16), reinterpret_cast<hipStream_t>(stream));
+    launch_exchange_w<E>(a, aligned(in, 16) && aligned(out, 16), two_shot, reinterpret_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
 }
 
@@ -504,6 +714,9 @@ extern "C" HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *
     info->flag_stride = kFlagStride;
     info->host_error = reinterpret_cast<volatile uint32_t *>(base + ch->error_off);
     info->host_abort = reinterpret_cast<volatile uint32_t *>(base + ch->abort_off);
+    info->algorithm = ch->algorithm;
+    info->host_reduced = base + ch->reduced_off;
+    info->host_flags2 = reinterpret_cast<volatile uint32_t *>(base + ch->flags2_off);
     return HR_OK;
 }
 

@@ -31,6 +31,9 @@ HR_MAX_WORLD = 8
 HR_DEFAULT_MAX_NUMEL = 131072
 HR_MAX_NUMEL_LIMIT = 1 << 29
 HR_DEFAULT_TIMEOUT_US = 1_000_000
+HR_ALGO_AUTO = 0
+HR_ALGO_ONE_SHOT = 1
+HR_ALGO_TWO_SHOT = 2
 
 # Every symbol include/hr.h declares.
 EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel_status",
@@ -54,7 +57,8 @@ class hr_channel_config(ctypes.Structure):
                 ("world_size", ctypes.c_int),
                 ("max_numel", ctypes.c_size_t),
                 ("num_blocks", ctypes.c_int),
-                ("timeout_us", ctypes.c_uint32)]
+                ("timeout_us", ctypes.c_uint32),
+                ("algorithm", ctypes.c_int)]
 
 
 class hr_admit_policy(ctypes.Structure):
@@ -76,7 +80,10 @@ class hr_channel_info(ctypes.Structure):
                 ("host_flags", ctypes.POINTER(ctypes.c_uint32)),
                 ("flag_stride", ctypes.c_size_t),
                 ("host_error", ctypes.POINTER(ctypes.c_uint32)),
-                ("host_abort", ctypes.POINTER(ctypes.c_uint32))]
+                ("host_abort", ctypes.POINTER(ctypes.c_uint32)),
+                ("algorithm", ctypes.c_int),
+                ("host_reduced", ctypes.c_void_p),
+                ("host_flags2", ctypes.POINTER(ctypes.c_uint32))]
 
 
 class HrError(RuntimeError):
@@ -130,9 +137,9 @@ def hr_status_str(status: int) -> str:
 
 
 def hr_create_channel(device: int = 0, world_size: int = 2, max_numel: int = 0,
-                      num_blocks: int = 0, timeout_us: int = 0) -> int:
+                      num_blocks: int = 0, timeout_us: int = 0, algorithm: int = 0) -> int:
     """Returns the channel handle (an integer address) or raises HrError."""
-    cfg = hr_channel_config(device, world_size, max_numel, num_blocks, timeout_us)
+    cfg = hr_channel_config(device, world_size, max_numel, num_blocks, timeout_us, algorithm)
     h = ctypes.c_void_p()
     st = load().hr_create_channel(ctypes.byref(cfg), ctypes.byref(h))
     if st != HR_OK:
@@ -259,9 +266,10 @@ class Channel:
     rank's call."""
 
     def __init__(self, device: int = 0, max_numel: int = 0, num_blocks: int = 0,
-                 timeout_us: int = 0, world_size: int = 2):
+                 timeout_us: int = 0, world_size: int = 2, algorithm: int = 0):
         self.world_size = world_size
-        self.handle = hr_create_channel(device, world_size, max_numel, num_blocks, timeout_us)
+        self.handle = hr_create_channel(device, world_size, max_numel, num_blocks, timeout_us,
+                                        algorithm)
 
     def allreduce(self, rank: int, inp, out, stream=None):
         """One rank's call; torch.float16 or torch.bfloat16 tensors."""

@@ -46,11 +46,16 @@ def check_all(outs, xbits, what):
         assert np.array_equal(got[0], got[r]), f"{what}: rank {r} differs from rank 0"
 
 
-@pytest.fixture(params=[3, 4, 8])
+ALGOS = {"one": hr.HR_ALGO_ONE_SHOT, "two": hr.HR_ALGO_TWO_SHOT}
+
+
+@pytest.fixture(params=[(3, "one"), (4, "one"), (8, "one"),
+                        (2, "two"), (3, "two"), (4, "two"), (8, "two")],
+                ids=lambda p: f"W{p[0]}-{p[1]}shot")
 def group(request):
-    W = request.param
+    W, algo = request.param
     streams = hr.LoopbackStreams(0, n=W)
-    ch = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
+    ch = hr.Channel(world_size=W, timeout_us=TIMEOUT_US, algorithm=ALGOS[algo])
     yield W, ch, streams
     torch.cuda.synchronize()
     ch.destroy()
@@ -102,10 +107,11 @@ def test_one_rank_on_the_other_access_path(group):
     check_all(outs, xb, f"W={W} mixed paths")
 
 
-def test_graph_replays_with_fresh_inputs():
+@pytest.mark.parametrize("algo", ["one", "two"])
+def test_graph_replays_with_fresh_inputs(algo):
     W, calls, n = 4, 5, 16_384
     streams = hr.LoopbackStreams(0, n=W)
-    ch = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
+    ch = hr.Channel(world_size=W, timeout_us=TIMEOUT_US, algorithm=ALGOS[algo])
     try:
         xin = [torch.empty((calls, n), dtype=torch.float16, device="cuda:0") for _ in range(W)]
         outs = [torch.empty_like(x) for x in xin]
@@ -137,10 +143,11 @@ def test_graph_replays_with_fresh_inputs():
         streams.destroy()
 
 
-def test_missing_rank_times_out_every_waiting_rank():
+@pytest.mark.parametrize("algo", ["one", "two"])
+def test_missing_rank_times_out_every_waiting_rank(algo):
     W = 4
     streams = hr.LoopbackStreams(0, n=W)
-    ch = hr.Channel(world_size=W, timeout_us=20_000)
+    ch = hr.Channel(world_size=W, timeout_us=20_000, algorithm=ALGOS[algo])
     try:
         xb = inputs.workload6(W, 1)
         xs = [to_dev(b) for b in xb]
@@ -160,3 +167,29 @@ def test_missing_rank_times_out_every_waiting_rank():
         torch.cuda.synchronize()
         ch.destroy()
         streams.destroy()
+
+
+def test_automatic_choice_mixes_algorithms_across_calls():
+    """Under HR_ALGO_AUTO a W = 4 channel takes the one-shot below 32768
+    values and the two-shot from there; alternating sizes alternate the
+    algorithm while the slot parity keeps advancing."""
+    W = 4
+    streams = hr.LoopbackStreams(0, n=W)
+    ch = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
+    try:
+        for call, n in enumerate([4096, 131_072, 32_767, 32_768, 9, 65_539]):
+            xb = [specials_mix(n, seed=500 + 10 * call + r) for r in range(W)]
+            xs = [to_dev(b) for b in xb]
+            outs = [torch.empty_like(x) for x in xs]
+            run_call(ch, xs, outs, streams)
+            check_all(outs, xb, f"auto call {call} n={n}")
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+        streams.destroy()
+
+
+def test_two_shot_needs_a_workgroup_per_shard():
+    with pytest.raises(hr.HrError) as ei:
+        hr.Channel(world_size=8, num_blocks=4, algorithm=hr.HR_ALGO_TWO_SHOT)
+    assert ei.value.status == hr.HR_ERR_INVALID_ARG
