@@ -214,6 +214,17 @@ HR_API hr_status hr_reduce_f16(const void *const *inputs, int G, void *out, size
                                hr_stream_t stream);
 
 /*
+ * hr_workspace_stride -- where to place G contributions of numel values in
+ * one device buffer for hr_reduce_f16 / _bf16: contribution g at
+ * base + g * stride values (stride = numel rounded up to 2 MiB, plus 4 KiB).
+ * Contributions a multiple of 2 MiB apart hit the same HBM banks at equal
+ * offsets; the 4 KiB shift spreads them, and the fold recognises the layout.
+ * The result does not depend on the layout; only the speed does.
+ * Pure host arithmetic.
+ */
+HR_API size_t hr_workspace_stride(size_t numel);
+
+/*
  * hr_reduce_bf16 / hr_allreduce_bf16 -- the same two operations on bfloat16
  * values (sign, 8-bit exponent, 7-bit fraction): left fold in rank order,
  * one bfloat16 rounding to nearest even per add, subnormals kept.  The SGLang

@@ -39,7 +39,8 @@ HR_ALGO_TWO_SHOT = 2
 EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel_status",
            "hr_channel_abort", "hr_channel_get_info", "hr_destroy", "hr_status_str",
            "hr_loopback_stream_create", "hr_loopback_stream_destroy",
-           "hr_reduce_bf16", "hr_allreduce_bf16", "hr_admit", "hr_route_str", "hr_decode_numel")
+           "hr_reduce_bf16", "hr_allreduce_bf16", "hr_admit", "hr_route_str", "hr_decode_numel",
+           "hr_workspace_stride")
 
 HR_ROUTE_HOST = 0
 HR_DECLINE_DISABLED = 1
@@ -123,8 +124,10 @@ def load() -> ctypes.CDLL:
     lib.hr_route_str.restype = ctypes.c_char_p
     lib.hr_decode_numel.argtypes = [ctypes.c_size_t, ctypes.c_size_t, ctypes.c_size_t]
     lib.hr_decode_numel.restype = ctypes.c_size_t
+    lib.hr_workspace_stride.argtypes = [ctypes.c_size_t]
+    lib.hr_workspace_stride.restype = ctypes.c_size_t
     for name in EXPORTS:
-        if name not in ("hr_status_str", "hr_route_str", "hr_decode_numel"):
+        if name not in ("hr_status_str", "hr_route_str", "hr_decode_numel", "hr_workspace_stride"):
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -216,6 +219,21 @@ def hr_route_str(route: int) -> str:
 
 def hr_decode_numel(max_batch: int, tokens_per_request: int, hidden: int) -> int:
     return load().hr_decode_numel(max_batch, tokens_per_request, hidden)
+
+
+def hr_workspace_stride(numel: int) -> int:
+    """Values between consecutive contributions in one fold workspace."""
+    return load().hr_workspace_stride(numel)
+
+
+def workspace(G: int, numel: int, dtype=None, device=0):
+    """A device buffer holding G contributions in the hr_workspace_stride
+    layout; returns (buffer, [view of contribution g])."""
+    import torch
+    dtype = torch.float16 if dtype is None else dtype
+    stride = hr_workspace_stride(numel)
+    buf = torch.empty(G * stride, dtype=dtype, device=torch.device("cuda", device))
+    return buf, [buf[g * stride:g * stride + numel] for g in range(G)]
 
 
 # ----------------------------------------------------- torch marshalling

@@ -68,3 +68,13 @@ def test_decode_sized_bound():
     assert hr.hr_decode_numel(64, 0, 6144) == 393_216          # 0 tokens counts as 1
     # the 1Cat-vLLM cap of 256 KiB is 32 decode tokens at hidden 4096
     assert hr.hr_decode_numel(32, 1, 4096) * 2 == 256 * 1024
+
+
+def test_workspace_stride():
+    mib2 = (2 << 20) // 2                        # 2 MiB in binary16 values
+    assert hr.hr_workspace_stride(16_777_216) == 16_777_216 + 2048
+    assert hr.hr_workspace_stride(1) == mib2 + 2048
+    assert hr.hr_workspace_stride(mib2 + 1) == 2 * mib2 + 2048
+    for n in (1, 4096, 393_216, 16_777_216, 9_000_001):
+        s = hr.hr_workspace_stride(n)
+        assert s >= n and (s * 2) % (2 << 20) == 4096

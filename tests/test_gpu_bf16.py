@@ -106,3 +106,15 @@ def test_one_channel_carries_both_types_across_calls():
         torch.cuda.synchronize()
         ch.destroy()
         streams.destroy()
+
+
+def test_workspace_layout_bf16():
+    G, n = 8, 1_000_003
+    xs = [inputs.gaussian_bf16(n, 1.0, 10, r) for r in range(G)]
+    buf, views = hr.workspace(G, n, dtype=torch.bfloat16)
+    for v, x in zip(views, xs):
+        v.copy_(to_dev_bf16(x))
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+    hr.reduce(views, out)
+    torch.cuda.synchronize()
+    assert_same_bits(to_host(out), oracle.fold_bf16(xs), "bf16 workspace", bf16=True)

@@ -162,3 +162,23 @@ def test_graph_capture_and_replay_with_new_inputs():
         g.replay()
         torch.cuda.synchronize()
         assert_same_bits(to_host(out), oracle.fold(xs), f"replay {call}")
+
+
+@pytest.mark.parametrize("G,n", [(8, 16_777_216), (8, 100_003), (8, 9), (4, 70_001), (16, 300_007)])
+def test_contributions_in_the_workspace_layout(G, n):
+    """Inputs placed hr_workspace_stride apart in one buffer (the layout the
+    eight-rank fold streams fastest from) fold to the same bits."""
+    xs = inputs.contributions(G, n, 1.0, workload=93) if n > 1000 else [specials_mix(n, 9 + r) for r in range(G)]
+    buf, views = hr.workspace(G, n)
+    for v, x in zip(views, xs):
+        v.copy_(to_dev(x))
+    out = torch.empty(n, dtype=torch.float16, device="cuda:0")
+    say(f"fold: workspace layout G={G} n={n}")
+    hr.reduce(views, out)
+    torch.cuda.synchronize()
+    ref = oracle.fold(xs, threads=8)[0] if n > 1_000_000 else oracle.fold(xs)
+    assert_same_bits(to_host(out), ref, f"workspace G={G} n={n}")
+    # in place, onto the first contribution
+    hr.reduce(views, views[0])
+    torch.cuda.synchronize()
+    assert_same_bits(to_host(views[0]), ref, f"workspace in place G={G} n={n}")
