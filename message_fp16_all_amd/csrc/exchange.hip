@@ -613,13 +613,20 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->abort_off = ch->error_off + kLine;
     ch->host_bytes = ch->abort_off + kLine;
 
+    // The call counters are zeroed on a private stream, so creating a channel
+    // never waits for other work on the device (such as another channel's
+    // kernels waiting for their peers).
     void *dev_view = nullptr;
-    if (hipHostMalloc(&ch->host_base, ch->host_bytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
-        hipHostGetDevicePointer(&dev_view, ch->host_base, 0) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void **>(&ch->dev_words),
-                  (static_cast<size_t>(world) * nb + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMemset(ch->dev_words, 0, (static_cast<size_t>(world) * nb + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
+    const size_t word_bytes = (static_cast<size_t>(world) * nb + 1) * sizeof(uint32_t);
+    hipStream_t init = nullptr;
+    bool ok = hipHostMalloc(&ch->host_base, ch->host_bytes, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
+              hipHostGetDevicePointer(&dev_view, ch->host_base, 0) == hipSuccess &&
+              hipMalloc(reinterpret_cast<void **>(&ch->dev_words), word_bytes) == hipSuccess &&
+              hipStreamCreateWithFlags(&init, hipStreamNonBlocking) == hipSuccess &&
+              hipMemsetAsync(ch->dev_words, 0, word_bytes, init) == hipSuccess &&
+              hipStreamSynchronize(init) == hipSuccess;
+    if (init != nullptr) (void)hipStreamDestroy(init);
+    if (!ok) {
         release(ch);
         return HR_ERR_HIP;
     }
