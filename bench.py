@@ -249,6 +249,9 @@ def eager_calls(c: Ctx, ch, x, o, streams, calls):
     return e0.elapsed_time(e1) * 1e-3 / calls
 
 
+ALGO_NAMES = {1: "one-shot", 2: "two-shot"}
+
+
 def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=200, gate_ms=None,
                       world=2, algorithm=0):
     torch, hr, inputs = c.torch, c.hr, c.inputs
@@ -260,6 +263,7 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
     ref = torch_fold(c, xb)
     ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=5_000_000, world_size=world,
                     algorithm=algorithm)
+    taken = ch.algorithm_for(n)
     try:
         for _ in range(warmup):
             for r in range(world):
@@ -285,8 +289,7 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
         ch.destroy()
     t_graph = elapsed / steps
     alg = (world + 1) * n * 2
-    two = algorithm == hr.HR_ALGO_TWO_SHOT or (algorithm == hr.HR_ALGO_AUTO and world >= 3
-                                                and n >= 32768)
+    two = taken == hr.HR_ALGO_TWO_SHOT
     if two:
         d2h = world * n * 2 + n * 2                 # contributions + folded shards
         h2d = 2 * (world - 1) * n * 2               # peers' shard parts + folded shards
@@ -294,7 +297,7 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
         d2h = world * n * 2                 # each rank publishes its slice once
         h2d = world * (world - 1) * n * 2   # each rank reads every peer's slice
     return {
-        "world": world, "algorithm": "two-shot" if two else "one-shot",
+        "world": world, "algorithm": ALGO_NAMES[taken],
         "tokens": tokens, "N": n, "bytes_per_call": alg,
         "graph_us": round(t_graph * 1e6, 3), "graph_GBps": round(alg / t_graph / 1e9, 2),
         "graph_frac_link": round(alg / t_graph / 1e9 / link_peak, 4),
@@ -671,6 +674,9 @@ def profile_kernel(which, reps):
     streams = hr.LoopbackStreams(0)
     ch = hr.Channel(timeout_us=2_000_000)
     info = ch.info()
+    algo = ch.algorithm_for(n)
+    if algo != hr.HR_ALGO_ONE_SHOT:
+        raise RuntimeError("the host-played peer follows the one-shot protocol")
     ref = (x0 + to_dev(x1b)).view(torch.int16)
     ok = True
     try:
@@ -690,7 +696,8 @@ def profile_kernel(which, reps):
         torch.cuda.synchronize()
         ch.destroy()
         streams.destroy()
-    log(f"exchange rank 0 against a host-played peer, N={n}: {reps} calls, bit_exact={ok}")
+    log(f"exchange ({ALGO_NAMES[algo]}) rank 0 against a host-played peer, N={n}: {reps} calls, "
+        f"bit_exact={ok}")
 
 
 # -------------------------------------------------------------------- main
@@ -725,11 +732,12 @@ def main():
         if want("exchange"):
             rows = []
             for t in c.inputs.TOKENS_EXCHANGE:
-                log(f"exchange tokens={t}")
-                r = exchange_workload(c, t, 500, 50, link_peak)
-                r.pop("_elapsed_s")
-                r.pop("_out")
-                rows.append(r)
+                for algo in (c.hr.HR_ALGO_AUTO, c.hr.HR_ALGO_TWO_SHOT):
+                    log(f"exchange tokens={t} algorithm={algo}")
+                    r = exchange_workload(c, t, 500, 50, link_peak, algorithm=algo)
+                    r.pop("_elapsed_s")
+                    r.pop("_out")
+                    rows.append(r)
             cfgs["exchange_2rank_host_slots"] = rows
             rows = []
             for w in (4, 8):

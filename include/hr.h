@@ -196,6 +196,17 @@ HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void *in, void 
                                   size_t numel, hr_stream_t stream);
 
 /*
+ * hr_exchange_algorithm -- which algorithm a call of numel values on this
+ * channel takes: HR_ALGO_ONE_SHOT or HR_ALGO_TWO_SHOT in *algorithm.  A
+ * function of the channel and numel only (not of a rank's buffers), which is
+ * why every rank of a call takes the same algorithm.  Host-only; enqueues
+ * nothing.
+ * Errors: HR_ERR_INVALID_ARG (null ch or algorithm), HR_ERR_TOO_LARGE
+ * (numel above the channel's max_numel).
+ */
+HR_API hr_status hr_exchange_algorithm(hr_channel ch, size_t numel, int *algorithm);
+
+/*
  * hr_reduce_f16 -- fold G contributions resident in device memory.
  *
  * out[i] = left fold of inputs[0][i] .. inputs[G-1][i] with one binary16

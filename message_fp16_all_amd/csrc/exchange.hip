@@ -692,6 +692,13 @@ extern "C" HR_API hr_status hr_allreduce_bf16(hr_channel ch, int rank, const voi
     return allreduce_impl<BF16>(ch, rank, in, out, numel, stream);
 }
 
+extern "C" HR_API hr_status hr_exchange_algorithm(hr_channel ch, size_t numel, int *algorithm) {
+    if (ch == nullptr || algorithm == nullptr) return HR_ERR_INVALID_ARG;
+    if (numel > ch->max_numel) return HR_ERR_TOO_LARGE;
+    *algorithm = use_two_shot(ch->algorithm, numel, ch->world_size, ch->nblocks) ? HR_ALGO_TWO_SHOT : HR_ALGO_ONE_SHOT;
+    return HR_OK;
+}
+
 extern "C" HR_API hr_status hr_channel_status(hr_channel ch) {
     if (ch == nullptr) return HR_ERR_INVALID_ARG;
     return static_cast<hr_status>(__atomic_load_n(

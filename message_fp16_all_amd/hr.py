@@ -40,7 +40,7 @@ EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel
            "hr_channel_abort", "hr_channel_get_info", "hr_destroy", "hr_status_str",
            "hr_loopback_stream_create", "hr_loopback_stream_destroy",
            "hr_reduce_bf16", "hr_allreduce_bf16", "hr_admit", "hr_route_str", "hr_decode_numel",
-           "hr_workspace_stride")
+           "hr_workspace_stride", "hr_exchange_algorithm")
 
 HR_ROUTE_HOST = 0
 HR_DECLINE_DISABLED = 1
@@ -111,6 +111,7 @@ def load() -> ctypes.CDLL:
     lib.hr_allreduce_bf16.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
     lib.hr_reduce_bf16.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.hr_channel_status.argtypes = [vp]
+    lib.hr_exchange_algorithm.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
     lib.hr_channel_abort.argtypes = [vp]
     lib.hr_channel_get_info.argtypes = [vp, ctypes.POINTER(hr_channel_info)]
     lib.hr_destroy.argtypes = [vp]
@@ -176,6 +177,15 @@ def hr_reduce_bf16(ptrs, G: int, out_ptr: int, numel: int, stream: int) -> int:
 
 def hr_channel_status(ch: int) -> int:
     return load().hr_channel_status(ch)
+
+
+def hr_exchange_algorithm(ch: int, numel: int) -> int:
+    """The HR_ALGO_* a call of numel values takes (raises HrError)."""
+    algo = ctypes.c_int(-1)
+    st = load().hr_exchange_algorithm(ch, numel, ctypes.byref(algo))
+    if st != HR_OK:
+        raise HrError(st, "hr_exchange_algorithm")
+    return algo.value
 
 
 def hr_channel_abort(ch: int) -> int:
@@ -310,6 +320,10 @@ class Channel:
 
     def info(self) -> hr_channel_info:
         return hr_channel_get_info(self.handle)
+
+    def algorithm_for(self, numel: int) -> int:
+        """The HR_ALGO_* a call of numel values on this channel takes."""
+        return hr_exchange_algorithm(self.handle, numel)
 
     def destroy(self):
         if self.handle:

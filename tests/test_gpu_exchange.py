@@ -36,9 +36,12 @@ def streams():
     ls.destroy()
 
 
-@pytest.fixture
-def channel():
-    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=TIMEOUT_US)
+# AUTO takes the one-shot for two ranks; the two-shot is also correct for two
+# ranks (each rank owns half of the values), so the whole two-rank battery runs
+# on both
+@pytest.fixture(params=[hr.HR_ALGO_AUTO, hr.HR_ALGO_TWO_SHOT], ids=["auto", "two-shot"])
+def channel(request):
+    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=TIMEOUT_US, algorithm=request.param)
     yield ch
     torch.cuda.synchronize()
     ch.destroy()
@@ -350,3 +353,24 @@ def test_graph_replays_with_odd_call_count_and_fresh_inputs(channel, streams):
         o0, o1 = torch.empty_like(x0), torch.empty_like(x1)
         loopback(channel, x0, x1, o0, o1, streams)
         check_pair(o0, o1, x0b, x1b, f"eager after replay {replay}")
+
+
+def test_algorithm_choice():
+    """Which algorithm a call takes, as the library reports it: a function of
+    the channel and numel only, whatever each rank's buffers."""
+    ch2 = hr.Channel(timeout_us=TIMEOUT_US)
+    ch2t = hr.Channel(timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_TWO_SHOT)
+    ch4 = hr.Channel(world_size=4, timeout_us=TIMEOUT_US)
+    ch4o = hr.Channel(world_size=4, timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_ONE_SHOT)
+    try:
+        assert ch2.algorithm_for(131_072) == hr.HR_ALGO_ONE_SHOT
+        assert ch2t.algorithm_for(1) == hr.HR_ALGO_TWO_SHOT
+        assert ch4.algorithm_for(32_767) == hr.HR_ALGO_ONE_SHOT
+        assert ch4.algorithm_for(32_768) == hr.HR_ALGO_TWO_SHOT
+        assert ch4o.algorithm_for(131_072) == hr.HR_ALGO_ONE_SHOT
+        with pytest.raises(hr.HrError) as ei:
+            ch2.algorithm_for(hr.HR_DEFAULT_MAX_NUMEL + 1)
+        assert ei.value.status == hr.HR_ERR_TOO_LARGE
+    finally:
+        for ch in (ch2, ch2t, ch4, ch4o):
+            ch.destroy()
