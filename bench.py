@@ -249,7 +249,7 @@ def eager_calls(c: Ctx, ch, x, o, streams, calls):
     return e0.elapsed_time(e1) * 1e-3 / calls
 
 
-ALGO_NAMES = {1: "one-shot", 2: "two-shot"}
+ALGO_NAMES = {1: "one-shot", 2: "two-shot", 3: "low-latency"}
 
 
 def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=200, gate_ms=None,
@@ -296,6 +296,8 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
     else:
         d2h = world * n * 2                 # each rank publishes its slice once
         h2d = world * (world - 1) * n * 2   # each rank reads every peer's slice
+        if taken == hr.HR_ALGO_LL:          # every 4 bytes of values travel with 4 of call number
+            d2h, h2d = 2 * d2h, 2 * h2d
     return {
         "world": world, "algorithm": ALGO_NAMES[taken],
         "tokens": tokens, "N": n, "bytes_per_call": alg,
@@ -313,25 +315,27 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
     }
 
 
-def workload5(c: Ctx, link_peak):
+def workload5(c: Ctx, link_peak, algorithm=0, gate_ms=None):
     torch, hr, inputs = c.torch, c.hr, c.inputs
     calls = 1000
     xb = inputs.workload5(calls=calls)
     n = xb.shape[2]
     xin = [c.to_dev(xb[r].reshape(-1)).view(calls, n) for r in range(2)]
     outs = [torch.empty_like(xin[r]) for r in range(2)]
-    ch = hr.Channel(timeout_us=5_000_000)
+    ch = hr.Channel(timeout_us=5_000_000, algorithm=algorithm)
+    taken = ch.algorithm_for(n)
     try:
         for k in range(4):
             ch.allreduce(0, xin[0][k], outs[0][k], c.streams[0])
             ch.allreduce(1, xin[1][k], outs[1][k], c.streams[1])
         torch.cuda.synchronize()
         graphs = [capture_calls(c, ch, r, xin[r], outs[r], c.streams[r], calls) for r in range(2)]
-        replay_pair(c, graphs, 15.0)
+        gate_ms = 15.0 if gate_ms is None else gate_ms
+        replay_pair(c, graphs, gate_ms)
         outs[0].zero_()
         outs[1].zero_()
         torch.cuda.synchronize()
-        elapsed, host_s = replay_pair(c, graphs, 15.0)
+        elapsed, host_s = replay_pair(c, graphs, gate_ms)
         if ch.status() != hr.HR_OK:
             raise RuntimeError(f"exchange failed: {hr.hr_status_str(ch.status())}")
         ref = torch_fold(c, [xb[0].reshape(-1), xb[1].reshape(-1)])
@@ -343,9 +347,10 @@ def workload5(c: Ctx, link_peak):
         ch.destroy()
     t = elapsed / calls
     alg = 3 * n * 2
-    return {"N": n, "calls": calls, "us_per_call": round(t * 1e6, 3),
+    return {"N": n, "calls": calls, "algorithm": ALGO_NAMES[taken], "us_per_call": round(t * 1e6, 3),
             "GBps": round(alg / t / 1e9, 2), "frac_link": round(alg / t / 1e9 / link_peak, 4),
-            "host_submit_ms": round(host_s * 1e3, 3), "bit_exact": exact}
+            "host_submit_ms": round(host_s * 1e3, 3), "gate_covered_submit": host_s * 1e3 < gate_ms,
+            "bit_exact": exact}
 
 
 # ------------------------------------------------------------ the HBM fold
@@ -732,17 +737,24 @@ def main():
         if want("exchange"):
             rows = []
             for t in c.inputs.TOKENS_EXCHANGE:
-                for algo in (c.hr.HR_ALGO_AUTO, c.hr.HR_ALGO_TWO_SHOT):
+                taken = set()
+                for algo in (c.hr.HR_ALGO_AUTO, c.hr.HR_ALGO_ONE_SHOT, c.hr.HR_ALGO_LL,
+                             c.hr.HR_ALGO_TWO_SHOT):
                     log(f"exchange tokens={t} algorithm={algo}")
                     r = exchange_workload(c, t, 500, 50, link_peak, algorithm=algo)
                     r.pop("_elapsed_s")
                     r.pop("_out")
-                    rows.append(r)
+                    if r["algorithm"] not in taken:       # AUTO first, then the others once
+                        taken.add(r["algorithm"])
+                        r["auto"] = algo == c.hr.HR_ALGO_AUTO
+                        rows.append(r)
             cfgs["exchange_2rank_host_slots"] = rows
             rows = []
             for w in (4, 8):
                 for t in (1, 8, 32):
-                    for algo in (c.hr.HR_ALGO_ONE_SHOT, c.hr.HR_ALGO_TWO_SHOT):
+                    for algo in (c.hr.HR_ALGO_ONE_SHOT, c.hr.HR_ALGO_TWO_SHOT, c.hr.HR_ALGO_LL):
+                        if algo == c.hr.HR_ALGO_LL and t * 4096 > 32768:
+                            continue
                         log(f"exchange world={w} tokens={t} algorithm={algo}")
                         r = exchange_workload(c, t, 300, 20, link_peak, eager_calls_n=50, world=w,
                                               algorithm=algo)
@@ -752,7 +764,10 @@ def main():
             cfgs["exchange_world_host_slots"] = rows
         if want("c5"):
             log("exchange graph of 1000 fresh calls, N=10240")
-            cfgs["exchange_graph_1000_calls_N10240"] = workload5(c, link_peak)
+            cfgs["exchange_graph_1000_calls_N10240"] = workload5(c, link_peak, gate_ms=args.gate_ms)
+            log("the same with the one-shot")
+            cfgs["exchange_graph_1000_calls_N10240_one_shot"] = workload5(c, link_peak, c.hr.HR_ALGO_ONE_SHOT,
+                                                                          gate_ms=args.gate_ms)
         if want("fold"):
             log("fold G=2 N=4096 with specials")
             cfgs["fold_G2_N4096_specials"] = fold_workload(c, "w1", c.inputs.workload1()[0])

@@ -95,12 +95,18 @@ typedef enum {
 /* Default watchdog for one wait on the peer, in microseconds. */
 #define HR_DEFAULT_TIMEOUT_US 1000000u
 
-/* Exchange algorithm of a channel (both produce the same bits). */
-#define HR_ALGO_AUTO 0      /* one-shot for two ranks and small payloads,
-                               two-shot for 3+ ranks from 32768 values    */
+/* Exchange algorithm of a channel (all produce the same bits). */
+#define HR_ALGO_AUTO 0      /* two ranks: low-latency up to 10240 values,
+                               one-shot above; 3+ ranks: one-shot, and
+                               two-shot from 32768 values                 */
 #define HR_ALGO_ONE_SHOT 1  /* every rank reads every peer's contribution */
 #define HR_ALGO_TWO_SHOT 2  /* shard owners fold, then everyone gathers;
                                needs num_blocks >= world_size             */
+#define HR_ALGO_LL 3        /* low-latency one-shot: every 8-byte word in
+                               host memory carries 4 bytes of values and
+                               the call number, so readers poll the data
+                               itself (no flags); twice the link bytes; up
+                               to 32768 values (larger calls: one-shot)   */
 
 typedef struct {
     int device;           /* HIP device ordinal the channel's kernels run on  */
@@ -139,6 +145,13 @@ typedef struct {
                                      [2 parity][slot_stride] binary16         */
     volatile uint32_t *host_flags2; /* two-shot reduced-shard flags, laid out
                                      like host_flags                          */
+    void *host_ll;                /* low-latency slots [2 parity][world]
+                                     [ll_stride] 16-byte words, each slot two
+                                     halves of ll_stride / 2 words; unit u of
+                                     a call is word u of the first half,
+                                     {v0v1, call, v2v3, call}, and word u of
+                                     the second, {v4v5, call, v6v7, call}     */
+    size_t ll_stride;             /* 16-byte words per low-latency slot       */
 } hr_channel_info;
 
 /*
@@ -166,7 +179,11 @@ HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out
  * One-shot algorithm (below); the two-shot (HR_ALGO_TWO_SHOT, or automatic
  * for larger groups and payloads) instead has each shard's owner fold that
  * shard in rank order and publish it, and every rank gather the others'
- * folded shards: less host-link traffic for W > 2, the same bits.
+ * folded shards: less host-link traffic for W > 2, the same bits.  The
+ * low-latency one-shot (HR_ALGO_LL, or automatic for two ranks up to 10240
+ * values) puts the call number into every 8-byte word it writes to host
+ * memory, so a peer polls the values themselves: no flag, no wait for
+ * acknowledgements, one host-link round trip less; the same bits again.
  *
  * Enqueues exactly one kernel on `stream`.  Its workgroups each own one
  * contiguous slice of the numel values: they copy the slice of `in` into this
@@ -197,10 +214,10 @@ HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void *in, void 
 
 /*
  * hr_exchange_algorithm -- which algorithm a call of numel values on this
- * channel takes: HR_ALGO_ONE_SHOT or HR_ALGO_TWO_SHOT in *algorithm.  A
- * function of the channel and numel only (not of a rank's buffers), which is
- * why every rank of a call takes the same algorithm.  Host-only; enqueues
- * nothing.
+ * channel takes: HR_ALGO_ONE_SHOT, HR_ALGO_TWO_SHOT or HR_ALGO_LL in
+ * *algorithm.  A function of the channel and numel only (not of a rank's
+ * buffers), which is why every rank of a call takes the same algorithm.
+ * Host-only; enqueues nothing.
  * Errors: HR_ERR_INVALID_ARG (null ch or algorithm), HR_ERR_TOO_LARGE
  * (numel above the channel's max_numel).
  */

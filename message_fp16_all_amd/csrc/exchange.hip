@@ -83,6 +83,8 @@ struct ExchArgs {
     uint32_t *flags;          // device view of the host flags (publish)
     uint32_t *flags2;         // device view of the host flags (reduced shard, two-shot)
     uint16_t *reduced;        // device view of the reduced-shard slots [2][stride] (two-shot)
+    u32x4 *ll;                // device view of the low-latency slots [2][W][ll_stride] (LL)
+    size_t ll_stride;         // 16-byte words per low-latency slot
     uint32_t *epochs;         // this rank's counters (HBM)
     uint32_t *dev_error;      // HBM
     uint32_t *host_error;     // device view of the host error word
@@ -448,6 +450,154 @@ __global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
     }
 }
 
+// Low-latency variant for small calls.  The one-shot's handshake costs two
+// host-link round trips beyond the data itself: a workgroup must see its
+// slot stores acknowledged before it raises its flag, and a peer must see
+// the flag before it may read the slot.  Here the data carries its own
+// readiness, in the manner of the low-latency protocol of NCCL and RCCL:
+// every 8-byte word written to host memory holds 4 bytes of values and the
+// call number e, so a reader that finds e in a word also holds that word's
+// values (8-byte aligned stores and loads are single accesses all the way to
+// host memory, so a word is never seen half written).  There is no flag, no
+// acknowledgement wait and no separate read; the price is twice the bytes on
+// the link, which is why only small calls take this path.
+//
+// Layout: LL slot [e & 1][q] holds two halves of ll_stride / 2 16-byte
+// words; for each 8-value unit u of the call, word u of the first half is
+// {v0v1, e, v2v3, e} and word u of the second {v4v5, e, v6v7, e}; the last
+// unit's missing values are zero.  One unit per lane: active workgroup b owns the
+// units [nunits*b/nact, nunits*(b+1)/nact).  Each lane publishes its unit,
+// then polls the two words of that unit in every peer's slot (all peers at
+// once) until every word carries e; after a barrier the workgroup folds left
+// in rank order and stores, or, if any lane of it timed out or saw an abort,
+// stores nothing.  A word of an earlier use of the parity holds e - 2, never
+// e; parity safety is the one-shot's argument, with "flag" read as "word".
+constexpr size_t kLLMaxNumel = 32768;      // values per call the LL slots hold
+constexpr size_t kLLAutoMaxNumel = 10240;  // automatic choice takes LL up to here (20 KiB)
+constexpr bool kLLAckFirst = true;         // first poll after the own words are acknowledged
+constexpr int kLLSleep = 8;                // s_sleep after a failed poll (x 64 clocks)
+
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
+    __shared__ uint32_t s_status;
+    const int b = blockIdx.x;
+    const int tid = static_cast<int>(threadIdx.x);
+    if (tid == 0) s_status = 0;
+    const uint32_t e = next_call(a, b);  // its barrier also orders s_status's reset
+    if (e == 0 || b >= a.nactive) return;
+    const int parity = static_cast<int>(e & 1u);
+    const int rank = a.rank;
+    const size_t nunits = (a.numel + kVecElems - 1) / kVecElems;
+    const size_t nvec = a.numel / kVecElems;
+    const size_t lo = nunits * static_cast<size_t>(b) / static_cast<size_t>(a.nactive);
+    const size_t hi = nunits * static_cast<size_t>(b + 1) / static_cast<size_t>(a.nactive);
+    const size_t u = lo + static_cast<size_t>(tid);
+    const bool has = u < hi;
+    const uint16_t *in16 = static_cast<const uint16_t *>(a.in);
+
+    // this lane's unit of `in` (zero past numel)
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (has) {
+        if (VEC && u < nvec) {
+            x = static_cast<const u32x4 *>(a.in)[u];
+        } else {
+#pragma unroll
+            for (int k = 0; k < kVecElems; ++k) {
+                const size_t i = u * kVecElems + static_cast<size_t>(k);
+                const uint32_t v = i < a.numel ? in16[i] : 0u;
+                x[k / 2] |= v << (16 * (k % 2));
+            }
+        }
+    }
+
+    __amdgpu_buffer_rsrc_t ll[W];
+#pragma unroll
+    for (int q = 0; q < W; ++q)
+        ll[q] = __builtin_amdgcn_make_buffer_rsrc(a.ll + static_cast<size_t>(W * parity + q) * a.ll_stride, 0,
+                                                  static_cast<int>(a.ll_stride * 16), kRawBufferDword3);
+    // word 0 of every unit, then word 1 of every unit: each store and load
+    // instruction covers 64 consecutive 16-byte words (whole lines; an
+    // interleaved layout makes partial-line writes to host memory, which the
+    // link carries at a small fraction of its rate)
+    const int off0 = static_cast<int>(u * 16), off1 = static_cast<int>((a.ll_stride / 2 + u) * 16);
+
+    // publish: both words of the unit, system-coherent, no wait
+    if (has) {
+        const u32x4 w0 = {x.x, e, x.y, e}, w1 = {x.z, e, x.w, e};
+        __builtin_amdgcn_raw_buffer_store_b128(w0, ll[rank], off0, 0, kSysCoherent);
+        __builtin_amdgcn_raw_buffer_store_b128(w1, ll[rank], off1, 0, kSysCoherent);
+    }
+
+    // the peers wrote theirs at about the same time: once this lane's own
+    // words are acknowledged, the first poll mostly finds the peers' words
+    if (kLLAckFirst) __builtin_amdgcn_s_waitcnt(0);
+
+    // gather: poll every pending peer's two words until both carry e
+    u32x4 got[W];
+    unsigned pending = has ? (((1u << W) - 1u) & ~(1u << rank)) : 0u;
+    uint32_t status = 0;
+    const long long t0 = wall_clock64();
+    for (;;) {
+        // all pending peers' loads, and the abort word, in flight at once
+        u32x4 w0[W], w1[W];
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            if ((pending >> q) & 1u) {
+                w0[q] = __builtin_amdgcn_raw_buffer_load_b128(ll[q], off0, 0, kSysCoherent);
+                w1[q] = __builtin_amdgcn_raw_buffer_load_b128(ll[q], off1, 0, kSysCoherent);
+            }
+        }
+        uint32_t ab = 0;
+        if (tid % 64 == 0) ab = __hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            if (((pending >> q) & 1u) && w0[q].y == e && w0[q].w == e && w1[q].y == e && w1[q].w == e) {
+                got[q] = u32x4{w0[q].x, w0[q].z, w1[q].x, w1[q].z};
+                pending &= ~(1u << q);
+            }
+        }
+        if (!__any(pending != 0u)) break;
+        if (__shfl(ab, 0) != 0) {
+            status = HR_ERR_ABORTED;
+            break;
+        }
+        if (static_cast<uint64_t>(wall_clock64() - t0) > a.timeout_ticks) {
+            status = HR_ERR_TIMEOUT;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(kLLSleep);
+    }
+    if (status != 0 && tid % 64 == 0) {
+        __hip_atomic_store(&s_status, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.host_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    __syncthreads();
+    if (s_status != 0 || !has) return;
+
+    // left fold in rank order, own values from registers
+    u32x4 acc = (rank == 0) ? x : got[0];
+#pragma unroll
+    for (int q = 1; q < W; ++q) acc = E::add8(acc, q == rank ? x : got[q]);
+    if (VEC && u < nvec) {
+        static_cast<u32x4 *>(a.out)[u] = acc;
+    } else {
+        uint16_t *out16 = static_cast<uint16_t *>(a.out);
+#pragma unroll
+        for (int k = 0; k < kVecElems; ++k) {
+            const size_t i = u * kVecElems + static_cast<size_t>(k);
+            if (i < a.numel) out16[i] = static_cast<uint16_t>(acc[k / 2] >> (16 * (k % 2)));
+        }
+    }
+}
+
+// Active workgroups of an LL call: one unit per lane.
+inline int active_blocks_ll(size_t numel) {
+    const size_t nunits = (numel + kVecElems - 1) / kVecElems;
+    const size_t want = (nunits + kExchThreads - 1) / kExchThreads;
+    return static_cast<int>(want < 1 ? 1 : want);
+}
+
 // Active workgroups of a two-shot call: W groups of m, m about one 16-byte
 // unit per lane of the shard, at least 1, at most nblocks / W.
 inline int active_blocks2(size_t numel, int nblocks, int world) {
@@ -474,23 +624,43 @@ inline int active_blocks(size_t numel, int nblocks, int world) {
     return static_cast<int>(want);
 }
 
-// Which algorithm a call takes: a function of the channel and numel only,
-// so every rank of a call takes the same one.  Automatic choice: the
-// one-shot for two ranks (the source's method) and for small payloads,
-// whose latency the second handshake would double; the two-shot for
-// groups of three or more above kTwoShotMinNumel values.
+// Groups of three or more take the two-shot from this many values under the
+// automatic choice; the second handshake doubles the latency of small calls.
 constexpr size_t kTwoShotMinNumel = 32768;
 
-inline bool use_two_shot(int algorithm, size_t numel, int world, int nblocks) {
-    if (nblocks < world) return false;
-    if (algorithm == HR_ALGO_TWO_SHOT) return true;
-    if (algorithm == HR_ALGO_ONE_SHOT) return false;
-    return world >= 3 && numel >= kTwoShotMinNumel;
+enum class Algo { one_shot, two_shot, ll };
+
+// The algorithm a call takes: a function of the channel and numel only (not
+// of a rank's buffers), so every rank of a call takes the same one.  LL needs
+// a call of at most kLLMaxNumel values (and one lane per unit); a call that
+// asks for an algorithm it cannot take gets the one-shot (same bits).
+// Automatic choice: for two ranks LL up to kLLAutoMaxNumel values and the
+// one-shot above; for three or more the one-shot, and the two-shot from
+// kTwoShotMinNumel (LL's readers poll every peer's data, which costs more
+// than it saves there).
+inline Algo choose_algo(int algorithm, size_t numel, int world, int nblocks) {
+    const bool ll_ok = numel <= kLLMaxNumel && active_blocks_ll(numel) <= nblocks;
+    const bool two_ok = nblocks >= world;
+    switch (algorithm) {
+        case HR_ALGO_ONE_SHOT: return Algo::one_shot;
+        case HR_ALGO_TWO_SHOT: return two_ok ? Algo::two_shot : Algo::one_shot;
+        case HR_ALGO_LL: return ll_ok ? Algo::ll : Algo::one_shot;
+        default: break;
+    }
+    if (world == 2 && ll_ok && numel <= kLLAutoMaxNumel) return Algo::ll;
+    return (two_ok && world >= 3 && numel >= kTwoShotMinNumel) ? Algo::two_shot : Algo::one_shot;
 }
 
 template <int W, class E>
-void launch_exchange(const ExchArgs &a, bool vec, bool two_shot, hipStream_t s) {
-    if (two_shot) {
+void launch_exchange(const ExchArgs &a, bool vec, Algo algo, hipStream_t s) {
+    if (algo == Algo::ll) {
+        if (vec)
+            hipLaunchKernelGGL((exchange_ll_k<W, true, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((exchange_ll_k<W, false, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+        return;
+    }
+    if (algo == Algo::two_shot) {
         if (vec)
             hipLaunchKernelGGL((exchange2_k<W, true, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
         else
@@ -504,15 +674,15 @@ void launch_exchange(const ExchArgs &a, bool vec, bool two_shot, hipStream_t s) 
 }
 
 template <class E>
-void launch_exchange_w(const ExchArgs &a, bool vec, bool two_shot, hipStream_t s) {
+void launch_exchange_w(const ExchArgs &a, bool vec, Algo algo, hipStream_t s) {
     switch (a.world) {
-        case 2: launch_exchange<2, E>(a, vec, two_shot, s); break;
-        case 3: launch_exchange<3, E>(a, vec, two_shot, s); break;
-        case 4: launch_exchange<4, E>(a, vec, two_shot, s); break;
-        case 5: launch_exchange<5, E>(a, vec, two_shot, s); break;
-        case 6: launch_exchange<6, E>(a, vec, two_shot, s); break;
-        case 7: launch_exchange<7, E>(a, vec, two_shot, s); break;
-        case 8: launch_exchange<8, E>(a, vec, two_shot, s); break;
+        case 2: launch_exchange<2, E>(a, vec, algo, s); break;
+        case 3: launch_exchange<3, E>(a, vec, algo, s); break;
+        case 4: launch_exchange<4, E>(a, vec, algo, s); break;
+        case 5: launch_exchange<5, E>(a, vec, algo, s); break;
+        case 6: launch_exchange<6, E>(a, vec, algo, s); break;
+        case 7: launch_exchange<7, E>(a, vec, algo, s); break;
+        case 8: launch_exchange<8, E>(a, vec, algo, s); break;
         default: break;
     }
 }
@@ -532,7 +702,7 @@ struct hr_channel_s {
     void *host_base;           // hipHostMalloc'ed region (host address)
     unsigned char *host_dev;   // the same region as seen by the device
     int algorithm;             // HR_ALGO_*
-    size_t flags_off, flags2_off, reduced_off, error_off, abort_off, host_bytes;
+    size_t flags_off, flags2_off, reduced_off, ll_off, ll_stride, error_off, abort_off, host_bytes;
     uint32_t *dev_words;       // hipMalloc: epochs[world * nblocks] then the error word
 };
 
@@ -564,7 +734,7 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     if (cfg == nullptr || out == nullptr) return HR_ERR_INVALID_ARG;
     if (cfg->world_size < 2 || cfg->world_size > kMaxWorld) return HR_ERR_UNSUPPORTED;
     if (cfg->device < 0 || cfg->num_blocks < 0) return HR_ERR_INVALID_ARG;
-    if (cfg->algorithm < HR_ALGO_AUTO || cfg->algorithm > HR_ALGO_TWO_SHOT) return HR_ERR_INVALID_ARG;
+    if (cfg->algorithm < HR_ALGO_AUTO || cfg->algorithm > HR_ALGO_LL) return HR_ERR_INVALID_ARG;
     const size_t max_numel = cfg->max_numel ? cfg->max_numel : HR_DEFAULT_MAX_NUMEL;
     // A slot is addressed by a buffer descriptor whose byte count and
     // offsets are 32-bit: keep one slot at or below 1 GiB.
@@ -609,7 +779,11 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->reduced_off = round_up(slot_bytes, kLine);
     ch->flags_off = ch->reduced_off + 2 * ch->stride * sizeof(uint16_t);
     ch->flags2_off = ch->flags_off + flag_bytes;
-    ch->error_off = ch->flags2_off + flag_bytes;
+    ch->ll_off = ch->flags2_off + flag_bytes;
+    // two 16-byte words per 8-value unit of the largest LL call
+    const size_t ll_max = max_numel < kLLMaxNumel ? max_numel : kLLMaxNumel;
+    ch->ll_stride = 2 * ((ll_max + kVecElems - 1) / kVecElems);
+    ch->error_off = ch->ll_off + round_up(2 * static_cast<size_t>(world) * ch->ll_stride * sizeof(u32x4), kLine);
     ch->abort_off = ch->error_off + kLine;
     ch->host_bytes = ch->abort_off + kLine;
 
@@ -664,6 +838,8 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
     a.flags = reinterpret_cast<uint32_t *>(ch->host_dev + ch->flags_off);
     a.flags2 = reinterpret_cast<uint32_t *>(ch->host_dev + ch->flags2_off);
     a.reduced = reinterpret_cast<uint16_t *>(ch->host_dev + ch->reduced_off);
+    a.ll = reinterpret_cast<u32x4 *>(ch->host_dev + ch->ll_off);
+    a.ll_stride = ch->ll_stride;
     a.epochs = ch->dev_words + static_cast<size_t>(rank) * ch->nblocks;
     a.dev_error = ch->dev_words + static_cast<size_t>(ch->world_size) * ch->nblocks;
     a.host_error = reinterpret_cast<uint32_t *>(ch->host_dev + ch->error_off);
@@ -672,11 +848,12 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
     a.rank = rank;
     a.world = ch->world_size;
     a.nblocks = ch->nblocks;
-    const bool two_shot = use_two_shot(ch->algorithm, numel, ch->world_size, ch->nblocks);
-    a.nactive = two_shot ? active_blocks2(numel, ch->nblocks, ch->world_size)
-                         : active_blocks(numel, ch->nblocks, ch->world_size);
+    const Algo algo = choose_algo(ch->algorithm, numel, ch->world_size, ch->nblocks);
+    a.nactive = algo == Algo::two_shot ? active_blocks2(numel, ch->nblocks, ch->world_size)
+                : algo == Algo::ll     ? active_blocks_ll(numel)
+                                       : active_blocks(numel, ch->nblocks, ch->world_size);
 
-    launch_exchange_w<E>(a, aligned(in, 16) && aligned(out, 16), two_shot, reinterpret_cast<hipStream_t>(stream));
+    launch_exchange_w<E>(a, aligned(in, 16) && aligned(out, 16), algo, reinterpret_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
 }
 
@@ -695,7 +872,11 @@ extern "C" HR_API hr_status hr_allreduce_bf16(hr_channel ch, int rank, const voi
 extern "C" HR_API hr_status hr_exchange_algorithm(hr_channel ch, size_t numel, int *algorithm) {
     if (ch == nullptr || algorithm == nullptr) return HR_ERR_INVALID_ARG;
     if (numel > ch->max_numel) return HR_ERR_TOO_LARGE;
-    *algorithm = use_two_shot(ch->algorithm, numel, ch->world_size, ch->nblocks) ? HR_ALGO_TWO_SHOT : HR_ALGO_ONE_SHOT;
+    switch (choose_algo(ch->algorithm, numel, ch->world_size, ch->nblocks)) {
+        case Algo::two_shot: *algorithm = HR_ALGO_TWO_SHOT; break;
+        case Algo::ll: *algorithm = HR_ALGO_LL; break;
+        default: *algorithm = HR_ALGO_ONE_SHOT; break;
+    }
     return HR_OK;
 }
 
@@ -731,6 +912,8 @@ extern "C" HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *
     info->algorithm = ch->algorithm;
     info->host_reduced = base + ch->reduced_off;
     info->host_flags2 = reinterpret_cast<volatile uint32_t *>(base + ch->flags2_off);
+    info->host_ll = base + ch->ll_off;
+    info->ll_stride = ch->ll_stride;
     return HR_OK;
 }
 

@@ -34,6 +34,7 @@ HR_DEFAULT_TIMEOUT_US = 1_000_000
 HR_ALGO_AUTO = 0
 HR_ALGO_ONE_SHOT = 1
 HR_ALGO_TWO_SHOT = 2
+HR_ALGO_LL = 3
 
 # Every symbol include/hr.h declares.
 EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel_status",
@@ -84,7 +85,9 @@ class hr_channel_info(ctypes.Structure):
                 ("host_abort", ctypes.POINTER(ctypes.c_uint32)),
                 ("algorithm", ctypes.c_int),
                 ("host_reduced", ctypes.c_void_p),
-                ("host_flags2", ctypes.POINTER(ctypes.c_uint32))]
+                ("host_flags2", ctypes.POINTER(ctypes.c_uint32)),
+                ("host_ll", ctypes.c_void_p),
+                ("ll_stride", ctypes.c_size_t)]
 
 
 class HrError(RuntimeError):

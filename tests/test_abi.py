@@ -92,7 +92,7 @@ def test_channel_validation_before_any_device_call():
     assert lib.hr_create_channel(ctypes.byref(cfg), ctypes.byref(h)) == hr.HR_ERR_INVALID_ARG
     cfg = hr.hr_channel_config(0, 2, hr.HR_MAX_NUMEL_LIMIT + 1, 0, 0)
     assert lib.hr_create_channel(ctypes.byref(cfg), ctypes.byref(h)) == hr.HR_ERR_INVALID_ARG
-    for algo in (-1, 3):
+    for algo in (-1, 4):
         cfg = hr.hr_channel_config(0, 2, 0, 0, 0, algo)
         assert lib.hr_create_channel(ctypes.byref(cfg), ctypes.byref(h)) == hr.HR_ERR_INVALID_ARG
     cfg = hr.hr_channel_config(0, 2, 0, -4, 0)

@@ -53,12 +53,14 @@ def test_torch_bf16_add_agrees():
     assert_same_bits(fold_gpu(xs), to_host(t), "bf16 vs torch", bf16=True)
 
 
+@pytest.mark.parametrize("algorithm", [hr.HR_ALGO_AUTO, hr.HR_ALGO_LL, hr.HR_ALGO_TWO_SHOT],
+                         ids=["auto", "ll", "two-shot"])
 @pytest.mark.parametrize("W", [2, 4])
-def test_exchange_bf16(W):
+def test_exchange_bf16(W, algorithm):
     streams = hr.LoopbackStreams(0, n=W)
-    ch = hr.Channel(world_size=W, timeout_us=2_000_000)
+    ch = hr.Channel(world_size=W, timeout_us=2_000_000, algorithm=algorithm)
     try:
-        for call, n in enumerate([131_072, 4096, 65_541, 9]):
+        for call, n in enumerate([131_072, 4096, 65_541, 9, 32_768, 12_345]):
             xb = [specials_mix_bf16(n, seed=1000 * call + 10 * W + r) for r in range(W)]
             xs = [to_dev_bf16(b) for b in xb]
             outs = [torch.empty_like(x) for x in xs]

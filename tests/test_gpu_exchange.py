@@ -36,10 +36,14 @@ def streams():
     ls.destroy()
 
 
-# AUTO takes the one-shot for two ranks; the two-shot is also correct for two
-# ranks (each rank owns half of the values), so the whole two-rank battery runs
-# on both
-@pytest.fixture(params=[hr.HR_ALGO_AUTO, hr.HR_ALGO_TWO_SHOT], ids=["auto", "two-shot"])
+# AUTO takes the low-latency one-shot up to 10240 values and the one-shot
+# above; the two-shot is also correct for two ranks (each rank owns half of
+# the values), so the whole two-rank battery runs on every algorithm
+ALGOS = [hr.HR_ALGO_AUTO, hr.HR_ALGO_ONE_SHOT, hr.HR_ALGO_TWO_SHOT, hr.HR_ALGO_LL]
+ALGO_IDS = ["auto", "one-shot", "two-shot", "ll"]
+
+
+@pytest.fixture(params=ALGOS, ids=ALGO_IDS)
 def channel(request):
     ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=TIMEOUT_US, algorithm=request.param)
     yield ch
@@ -194,8 +198,9 @@ def test_skewed_arrival(channel, streams, first):
     check_pair(out[0], out[1], x0b, x1b, f"skew first={first}")
 
 
-def test_peer_never_arrives_times_out(streams):
-    ch = hr.Channel(timeout_us=20_000)
+@pytest.mark.parametrize("algorithm", [hr.HR_ALGO_ONE_SHOT, hr.HR_ALGO_LL], ids=["one-shot", "ll"])
+def test_peer_never_arrives_times_out(streams, algorithm):
+    ch = hr.Channel(timeout_us=20_000, algorithm=algorithm)
     try:
         x = to_dev(inputs.workload2(4)[0])
         out = torch.full_like(x, 3.0)
@@ -217,8 +222,9 @@ def test_peer_never_arrives_times_out(streams):
         ch.destroy()
 
 
-def test_abort_releases_a_waiting_kernel(streams):
-    ch = hr.Channel(timeout_us=5_000_000)
+@pytest.mark.parametrize("algorithm", [hr.HR_ALGO_ONE_SHOT, hr.HR_ALGO_LL], ids=["one-shot", "ll"])
+def test_abort_releases_a_waiting_kernel(streams, algorithm):
+    ch = hr.Channel(timeout_us=5_000_000, algorithm=algorithm)
     try:
         x = to_dev(inputs.workload2(4)[0])
         out = torch.full_like(x, 3.0)
@@ -241,7 +247,7 @@ def test_host_acts_as_the_peer(streams):
     """Integrity of both directions of the host link: the kernel's slot writes
     are read back by the CPU bit for bit, and values the CPU writes into the
     peer's slot (then flags) are what the kernel adds."""
-    ch = hr.Channel(timeout_us=TIMEOUT_US)
+    ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_ONE_SHOT)
     try:
         info = ch.info()
         n = 65_536 + 3
@@ -268,6 +274,55 @@ def test_host_acts_as_the_peer(streams):
         raised = [info.host_flags[(0 * info.num_blocks + b) * info.flag_stride]
                   for b in range(info.num_blocks)]
         assert raised == [1] * active + [0] * (info.num_blocks - active)
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+
+
+def ll_words(bits, call, half_words):
+    """The low-latency slot image of one contribution: two halves of
+    half_words 16-byte words; unit u (8 values, the last one zero-padded) is
+    word u of the first half, {v0v1, call, v2v3, call}, and word u of the
+    second, {v4v5, call, v6v7, call}."""
+    n = bits.size
+    units = -(-n // 8)
+    v = np.zeros(units * 8, np.uint16)
+    v[:n] = bits
+    pairs = v.view(np.uint32).reshape(units, 4)
+    img = np.zeros((2, half_words, 4), np.uint32)
+    img[0, :units, 0], img[0, :units, 2] = pairs[:, 0], pairs[:, 1]
+    img[1, :units, 0], img[1, :units, 2] = pairs[:, 2], pairs[:, 3]
+    img[:, :units, 1] = call
+    img[:, :units, 3] = call
+    return img, units
+
+
+@pytest.mark.parametrize("n", [4096, 9, 32_768])
+def test_host_acts_as_the_peer_ll(streams, n):
+    """The low-latency protocol seen from the host: the CPU writes the peer's
+    words for call 1 (values and call number) into the parity-1 slot; the
+    kernel adds them, and its own slot holds exactly the word image of its
+    contribution."""
+    ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_LL)
+    try:
+        info = ch.info()
+        assert ch.algorithm_for(n) == hr.HR_ALGO_LL
+        x0b, x1b = specials_mix(n, 45), specials_mix(n, 46)
+        x0 = to_dev(x0b)
+        out0 = torch.empty_like(x0)
+        slot_bytes = info.ll_stride * 16
+        half = info.ll_stride // 2
+        peer, _ = ll_words(x1b, 1, half)
+        ctypes.memmove(info.host_ll + (2 * 1 + 1) * slot_bytes, peer.ctypes.data, peer.nbytes)
+        torch.cuda.synchronize()
+        ch.allreduce(0, x0, out0, streams[0])          # call 1 -> parity 1
+        streams[0].synchronize()
+        assert ch.status() == hr.HR_OK
+        assert_same_bits(to_host(out0), oracle.add(x0b, x1b), "host peer, LL")
+        own, units = ll_words(x0b, 1, half)
+        seen = np.frombuffer(ctypes.string_at(info.host_ll + (2 * 1 + 0) * slot_bytes, slot_bytes),
+                             dtype=np.uint32).reshape(2, half, 4)
+        assert np.array_equal(seen[:, :units], own[:, :units])
     finally:
         torch.cuda.synchronize()
         ch.destroy()
@@ -360,17 +415,25 @@ def test_algorithm_choice():
     the channel and numel only, whatever each rank's buffers."""
     ch2 = hr.Channel(timeout_us=TIMEOUT_US)
     ch2t = hr.Channel(timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_TWO_SHOT)
+    ch2l = hr.Channel(timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_LL)
     ch4 = hr.Channel(world_size=4, timeout_us=TIMEOUT_US)
     ch4o = hr.Channel(world_size=4, timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_ONE_SHOT)
+    chs = (ch2, ch2t, ch2l, ch4, ch4o)
     try:
+        assert ch2.algorithm_for(1) == hr.HR_ALGO_LL
+        assert ch2.algorithm_for(10_240) == hr.HR_ALGO_LL
+        assert ch2.algorithm_for(10_241) == hr.HR_ALGO_ONE_SHOT
         assert ch2.algorithm_for(131_072) == hr.HR_ALGO_ONE_SHOT
         assert ch2t.algorithm_for(1) == hr.HR_ALGO_TWO_SHOT
+        assert ch2l.algorithm_for(32_768) == hr.HR_ALGO_LL
+        assert ch2l.algorithm_for(32_769) == hr.HR_ALGO_ONE_SHOT
+        assert ch4.algorithm_for(10_240) == hr.HR_ALGO_ONE_SHOT
         assert ch4.algorithm_for(32_767) == hr.HR_ALGO_ONE_SHOT
         assert ch4.algorithm_for(32_768) == hr.HR_ALGO_TWO_SHOT
-        assert ch4o.algorithm_for(131_072) == hr.HR_ALGO_ONE_SHOT
+        assert ch4o.algorithm_for(4096) == hr.HR_ALGO_ONE_SHOT
         with pytest.raises(hr.HrError) as ei:
             ch2.algorithm_for(hr.HR_DEFAULT_MAX_NUMEL + 1)
         assert ei.value.status == hr.HR_ERR_TOO_LARGE
     finally:
-        for ch in (ch2, ch2t, ch4, ch4o):
+        for ch in chs:
             ch.destroy()

@@ -46,12 +46,13 @@ def check_all(outs, xbits, what):
         assert np.array_equal(got[0], got[r]), f"{what}: rank {r} differs from rank 0"
 
 
-ALGOS = {"one": hr.HR_ALGO_ONE_SHOT, "two": hr.HR_ALGO_TWO_SHOT}
+ALGOS = {"one": hr.HR_ALGO_ONE_SHOT, "two": hr.HR_ALGO_TWO_SHOT, "ll": hr.HR_ALGO_LL}
 
 
 @pytest.fixture(params=[(3, "one"), (4, "one"), (8, "one"),
-                        (2, "two"), (3, "two"), (4, "two"), (8, "two")],
-                ids=lambda p: f"W{p[0]}-{p[1]}shot")
+                        (2, "two"), (3, "two"), (4, "two"), (8, "two"),
+                        (3, "ll"), (4, "ll"), (8, "ll")],
+                ids=lambda p: f"W{p[0]}-{p[1]}")
 def group(request):
     W, algo = request.param
     streams = hr.LoopbackStreams(0, n=W)
@@ -107,7 +108,7 @@ def test_one_rank_on_the_other_access_path(group):
     check_all(outs, xb, f"W={W} mixed paths")
 
 
-@pytest.mark.parametrize("algo", ["one", "two"])
+@pytest.mark.parametrize("algo", ["one", "two", "ll"])
 def test_graph_replays_with_fresh_inputs(algo):
     W, calls, n = 4, 5, 16_384
     streams = hr.LoopbackStreams(0, n=W)
@@ -143,7 +144,7 @@ def test_graph_replays_with_fresh_inputs(algo):
         streams.destroy()
 
 
-@pytest.mark.parametrize("algo", ["one", "two"])
+@pytest.mark.parametrize("algo", ["one", "two", "ll"])
 def test_missing_rank_times_out_every_waiting_rank(algo):
     W = 4
     streams = hr.LoopbackStreams(0, n=W)
@@ -177,7 +178,7 @@ def test_automatic_choice_mixes_algorithms_across_calls():
     streams = hr.LoopbackStreams(0, n=W)
     ch = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
     try:
-        for call, n in enumerate([4096, 131_072, 32_767, 32_768, 9, 65_539]):
+        for call, n in enumerate([4096, 131_072, 32_767, 32_768, 9, 65_539, 10_241, 10_240]):
             xb = [specials_mix(n, seed=500 + 10 * call + r) for r in range(W)]
             xs = [to_dev(b) for b in xb]
             outs = [torch.empty_like(x) for x in xs]
