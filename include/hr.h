@@ -134,16 +134,16 @@ typedef struct {
     void *host_slots;             /* host address of the slot region:
                                      [2 parity][world][slot_stride] binary16  */
     size_t slot_stride;           /* elements per slot (>= max_numel)         */
-    volatile uint32_t *host_flags; /* host address of the ready flags:
-                                     flag of (rank r, block b) at index
-                                     (r * num_blocks + b) * flag_stride       */
-    size_t flag_stride;           /* uint32 words between consecutive flags   */
+    volatile uint64_t *host_flags; /* host address of the ready flags (64-bit
+                                     call numbers): flag of (rank r, block b)
+                                     at index (r * num_blocks + b) * flag_stride */
+    size_t flag_stride;           /* uint64 words between consecutive flags   */
     volatile uint32_t *host_error; /* sticky asynchronous status word         */
     volatile uint32_t *host_abort; /* nonzero = cancel waits                  */
     int algorithm;                /* HR_ALGO_* the channel was created with  */
     void *host_reduced;           /* two-shot reduced-shard slots
                                      [2 parity][slot_stride] binary16         */
-    volatile uint32_t *host_flags2; /* two-shot reduced-shard flags, laid out
+    volatile uint64_t *host_flags2; /* two-shot reduced-shard flags, laid out
                                      like host_flags                          */
     void *host_ll;                /* low-latency slots [2 parity][world]
                                      [ll_stride] 16-byte words, each slot two
@@ -152,6 +152,13 @@ typedef struct {
                                      {v0v1, call, v2v3, call}, and word u of
                                      the second, {v4v5, call, v6v7, call}     */
     size_t ll_stride;             /* 16-byte words per low-latency slot       */
+    uint64_t *dev_epochs;         /* device address of the call counters
+                                     [world][num_blocks]: the last call number
+                                     each rank's workgroup took.  Call numbers
+                                     run 1, 2, 3, ... skipping every value
+                                     whose low 32 bits are zero; a flag holds
+                                     the full number, a low-latency word its
+                                     low 32 bits.                             */
 } hr_channel_info;
 
 /*

@@ -20,11 +20,11 @@
 //   host (pinned, device-mapped, fine-grained/coherent):
 //     slots  [2 parity][W rank][stride] binary16 -- the 2 x world x numel
 //            workspace of the SGLang page's "Modifications" section
-//     flags  [W rank][nblocks], one 128-byte line each: the call number of
-//            the last chunk that workgroup published
+//     flags  [W rank][nblocks], one 128-byte line each: the (64-bit) call
+//            number of the last chunk that workgroup published
 //     error word, abort word (one line each)
-//   device (HBM): epoch[W rank][nblocks] -- per-workgroup call counter,
-//     device error word.
+//   device (HBM): epoch[W rank][nblocks] -- per-workgroup 64-bit call
+//     counter, device error word.
 //
 // Every launch has the channel's fixed workgroup count; each workgroup
 // advances its call counter, so parity is uniform across a call.  Only the
@@ -72,7 +72,7 @@ constexpr int kExchUnroll = 4;                    // units per lane per publish 
 constexpr int kMaxWorld = 8;
 constexpr int kMinActivePolls = 16;                // W * minimum active workgroups
 constexpr size_t kLine = 128;                     // bytes per flag / word line
-constexpr size_t kFlagStride = kLine / sizeof(uint32_t);
+constexpr size_t kFlagStride = kLine / sizeof(uint64_t);  // flags are 64-bit call numbers
 
 struct ExchArgs {
     const void *in;
@@ -80,12 +80,12 @@ struct ExchArgs {
     size_t numel;
     uint16_t *slots;          // device view of the host slot region
     size_t stride;            // values per slot
-    uint32_t *flags;          // device view of the host flags (publish)
-    uint32_t *flags2;         // device view of the host flags (reduced shard, two-shot)
+    uint64_t *flags;          // device view of the host flags (publish)
+    uint64_t *flags2;         // device view of the host flags (reduced shard, two-shot)
     uint16_t *reduced;        // device view of the reduced-shard slots [2][stride] (two-shot)
     u32x4 *ll;                // device view of the low-latency slots [2][W][ll_stride] (LL)
     size_t ll_stride;         // 16-byte words per low-latency slot
-    uint32_t *epochs;         // this rank's counters (HBM)
+    uint64_t *epochs;         // this rank's call counters (HBM)
     uint32_t *dev_error;      // HBM
     uint32_t *host_error;     // device view of the host error word
     const uint32_t *abort_w;  // device view of the host abort word
@@ -149,18 +149,18 @@ struct HostIO<uint16_t> {
 // is set, or the watchdog expires.  Returns 0, HR_ERR_ABORTED or
 // HR_ERR_TIMEOUT, the same in every lane of the wave; lane 0 records an
 // error in both error words.
-__device__ __forceinline__ uint32_t wait_flags(const ExchArgs &a, const uint32_t *flag_base, int b, uint32_t e,
+__device__ __forceinline__ uint32_t wait_flags(const ExchArgs &a, const uint64_t *flag_base, int b, uint64_t e,
                                                unsigned mask) {
     const int lane = threadIdx.x;
     const bool polls = lane < kMaxWorld && ((mask >> lane) & 1u);
-    const uint32_t *pf = flag_base + (static_cast<size_t>(polls ? lane : 0) * a.nblocks + b) * kFlagStride;
+    const uint64_t *pf = flag_base + (static_cast<size_t>(polls ? lane : 0) * a.nblocks + b) * kFlagStride;
     bool done = !polls;
     uint32_t status = 0;
     const long long t0 = wall_clock64();
     for (;;) {
         if (!done) {
-            const uint32_t f = __hip_atomic_load(pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            done = static_cast<int32_t>(f - e) >= 0;
+            const uint64_t f = __hip_atomic_load(pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            done = static_cast<int64_t>(f - e) >= 0;
         }
         if (__all(done)) break;
         uint32_t ab = 0;
@@ -182,14 +182,26 @@ __device__ __forceinline__ uint32_t wait_flags(const ExchArgs &a, const uint32_t
     return status;
 }
 
+// Call numbers run 1, 2, 3, ... and skip every value whose low 32 bits are
+// zero (two values at a time, so the parity keeps alternating).  They are
+// 64-bit, so a flag that a workgroup has not raised for any number of calls
+// still compares below the current call; and the low 32 bits, which the
+// low-latency words carry, are never zero, so a word never written (zero)
+// is never taken for a current one.
+__device__ __forceinline__ uint64_t next_call_number(uint64_t prev) {
+    const uint64_t e = prev + 1u;
+    return static_cast<uint32_t>(e) == 0u ? e + 2u : e;
+}
+
 // Advance this workgroup's call counter (every launched workgroup does, so a
 // rank's workgroups agree on the slot parity); returns the call number e, or
 // 0 when the channel already holds an error.
-__device__ __forceinline__ uint32_t next_call(const ExchArgs &a, int b) {
-    __shared__ uint32_t s_epoch;
+__device__ __forceinline__ uint64_t next_call(const ExchArgs &a, int b) {
+    __shared__ uint64_t s_epoch;
     if (threadIdx.x == 0) {
         const uint32_t err = __hip_atomic_load(a.dev_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t e = __hip_atomic_load(&a.epochs[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        const uint64_t e =
+            next_call_number(__hip_atomic_load(&a.epochs[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         if (err == 0) __hip_atomic_store(&a.epochs[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_epoch = err == 0 ? e : 0u;
     }
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
 
-    const uint32_t e = next_call(a, b);
+    const uint64_t e = next_call(a, b);
     if (e == 0 || b >= a.nactive) return;
     const int parity = static_cast<int>(e & 1u);
     const int rank = a.rank;
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
 
-    const uint32_t e = next_call(a, b);
+    const uint64_t e = next_call(a, b);
     if (e == 0 || b >= a.nactive) return;
     const int parity = static_cast<int>(e & 1u);
     const int rank = a.rank;
@@ -483,9 +495,10 @@ __global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
     const int b = blockIdx.x;
     const int tid = static_cast<int>(threadIdx.x);
     if (tid == 0) s_status = 0;
-    const uint32_t e = next_call(a, b);  // its barrier also orders s_status's reset
-    if (e == 0 || b >= a.nactive) return;
-    const int parity = static_cast<int>(e & 1u);
+    const uint64_t e64 = next_call(a, b);  // its barrier also orders s_status's reset
+    if (e64 == 0 || b >= a.nactive) return;
+    const uint32_t e = static_cast<uint32_t>(e64);  // the words carry the low 32 bits (never 0)
+    const int parity = static_cast<int>(e64 & 1u);
     const int rank = a.rank;
     const size_t nunits = (a.numel + kVecElems - 1) / kVecElems;
     const size_t nvec = a.numel / kVecElems;
@@ -703,7 +716,9 @@ struct hr_channel_s {
     unsigned char *host_dev;   // the same region as seen by the device
     int algorithm;             // HR_ALGO_*
     size_t flags_off, flags2_off, reduced_off, ll_off, ll_stride, error_off, abort_off, host_bytes;
-    uint32_t *dev_words;       // hipMalloc: epochs[world * nblocks] then the error word
+    void *dev_base;            // hipMalloc: epochs[world][nblocks] (uint64), then the error word
+    uint64_t *dev_epochs;
+    uint32_t *dev_error;
 };
 
 namespace {
@@ -724,7 +739,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 void release(hr_channel ch) {
     if (ch->host_base) (void)hipHostFree(ch->host_base);
-    if (ch->dev_words) (void)hipFree(ch->dev_words);
+    if (ch->dev_base) (void)hipFree(ch->dev_base);
     delete ch;
 }
 
@@ -791,13 +806,13 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     // never waits for other work on the device (such as another channel's
     // kernels waiting for their peers).
     void *dev_view = nullptr;
-    const size_t word_bytes = (static_cast<size_t>(world) * nb + 1) * sizeof(uint32_t);
+    const size_t word_bytes = static_cast<size_t>(world) * nb * sizeof(uint64_t) + sizeof(uint64_t);
     hipStream_t init = nullptr;
     bool ok = hipHostMalloc(&ch->host_base, ch->host_bytes, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
               hipHostGetDevicePointer(&dev_view, ch->host_base, 0) == hipSuccess &&
-              hipMalloc(reinterpret_cast<void **>(&ch->dev_words), word_bytes) == hipSuccess &&
+              hipMalloc(&ch->dev_base, word_bytes) == hipSuccess &&
               hipStreamCreateWithFlags(&init, hipStreamNonBlocking) == hipSuccess &&
-              hipMemsetAsync(ch->dev_words, 0, word_bytes, init) == hipSuccess &&
+              hipMemsetAsync(ch->dev_base, 0, word_bytes, init) == hipSuccess &&
               hipStreamSynchronize(init) == hipSuccess;
     if (init != nullptr) (void)hipStreamDestroy(init);
     if (!ok) {
@@ -805,6 +820,8 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
         return HR_ERR_HIP;
     }
     ch->host_dev = static_cast<unsigned char *>(dev_view);
+    ch->dev_epochs = static_cast<uint64_t *>(ch->dev_base);
+    ch->dev_error = reinterpret_cast<uint32_t *>(ch->dev_epochs + static_cast<size_t>(world) * nb);
     std::memset(ch->host_base, 0, ch->host_bytes);
     __atomic_thread_fence(__ATOMIC_SEQ_CST);
     *out = ch;
@@ -835,13 +852,13 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
     a.numel = numel;
     a.slots = reinterpret_cast<uint16_t *>(ch->host_dev);
     a.stride = ch->stride;
-    a.flags = reinterpret_cast<uint32_t *>(ch->host_dev + ch->flags_off);
-    a.flags2 = reinterpret_cast<uint32_t *>(ch->host_dev + ch->flags2_off);
+    a.flags = reinterpret_cast<uint64_t *>(ch->host_dev + ch->flags_off);
+    a.flags2 = reinterpret_cast<uint64_t *>(ch->host_dev + ch->flags2_off);
     a.reduced = reinterpret_cast<uint16_t *>(ch->host_dev + ch->reduced_off);
     a.ll = reinterpret_cast<u32x4 *>(ch->host_dev + ch->ll_off);
     a.ll_stride = ch->ll_stride;
-    a.epochs = ch->dev_words + static_cast<size_t>(rank) * ch->nblocks;
-    a.dev_error = ch->dev_words + static_cast<size_t>(ch->world_size) * ch->nblocks;
+    a.epochs = ch->dev_epochs + static_cast<size_t>(rank) * ch->nblocks;
+    a.dev_error = ch->dev_error;
     a.host_error = reinterpret_cast<uint32_t *>(ch->host_dev + ch->error_off);
     a.abort_w = reinterpret_cast<const uint32_t *>(ch->host_dev + ch->abort_off);
     a.timeout_ticks = ch->timeout_ticks;
@@ -905,14 +922,15 @@ extern "C" HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *
     info->timeout_us = ch->timeout_us;
     info->host_slots = base;
     info->slot_stride = ch->stride;
-    info->host_flags = reinterpret_cast<volatile uint32_t *>(base + ch->flags_off);
+    info->host_flags = reinterpret_cast<volatile uint64_t *>(base + ch->flags_off);
     info->flag_stride = kFlagStride;
     info->host_error = reinterpret_cast<volatile uint32_t *>(base + ch->error_off);
     info->host_abort = reinterpret_cast<volatile uint32_t *>(base + ch->abort_off);
     info->algorithm = ch->algorithm;
     info->host_reduced = base + ch->reduced_off;
-    info->host_flags2 = reinterpret_cast<volatile uint32_t *>(base + ch->flags2_off);
+    info->host_flags2 = reinterpret_cast<volatile uint64_t *>(base + ch->flags2_off);
     info->host_ll = base + ch->ll_off;
+    info->dev_epochs = ch->dev_epochs;
     info->ll_stride = ch->ll_stride;
     return HR_OK;
 }

@@ -79,15 +79,16 @@ class hr_channel_info(ctypes.Structure):
                 ("timeout_us", ctypes.c_uint32),
                 ("host_slots", ctypes.c_void_p),
                 ("slot_stride", ctypes.c_size_t),
-                ("host_flags", ctypes.POINTER(ctypes.c_uint32)),
+                ("host_flags", ctypes.POINTER(ctypes.c_uint64)),
                 ("flag_stride", ctypes.c_size_t),
                 ("host_error", ctypes.POINTER(ctypes.c_uint32)),
                 ("host_abort", ctypes.POINTER(ctypes.c_uint32)),
                 ("algorithm", ctypes.c_int),
                 ("host_reduced", ctypes.c_void_p),
-                ("host_flags2", ctypes.POINTER(ctypes.c_uint32)),
+                ("host_flags2", ctypes.POINTER(ctypes.c_uint64)),
                 ("host_ll", ctypes.c_void_p),
-                ("ll_stride", ctypes.c_size_t)]
+                ("ll_stride", ctypes.c_size_t),
+                ("dev_epochs", ctypes.c_void_p)]
 
 
 class HrError(RuntimeError):

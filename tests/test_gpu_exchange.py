@@ -437,3 +437,65 @@ def test_algorithm_choice():
     finally:
         for ch in chs:
             ch.destroy()
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (the library torch loaded),
+    found by path so that no second copy is loaded."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64.so" in path and path.startswith("/"):
+                lib = ctypes.CDLL(path)
+                lib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+                return lib
+    raise RuntimeError("libamdhip64 is not loaded")
+
+
+def _counters(ch, value=None):
+    """Read (or first set) every rank's per-workgroup call counters."""
+    info = ch.info()
+    n = info.world_size * info.num_blocks
+    arr = (ctypes.c_uint64 * n)()
+    hip = _hip_runtime()
+    torch.cuda.synchronize()
+    if value is not None:
+        for i in range(n):
+            arr[i] = value
+        assert hip.hipMemcpy(info.dev_epochs, ctypes.addressof(arr), ctypes.sizeof(arr), 1) == 0
+    assert hip.hipMemcpy(ctypes.addressof(arr), info.dev_epochs, ctypes.sizeof(arr), 2) == 0
+    torch.cuda.synchronize()
+    return list(arr)
+
+
+def _next_call_number(prev):
+    e = prev + 1
+    return e + 2 if e % (1 << 32) == 0 else e
+
+
+@pytest.mark.parametrize("start", [(1 << 31) + 5, (1 << 32) - 3, (1 << 33) - 2])
+def test_call_numbers_far_from_zero(streams, start):
+    """Long-running channels: with every call counter set to `start` on a
+    fresh channel (all flags and low-latency words still zero, as for
+    workgroups and units a long-running process has never used), a sequence
+    of calls of every algorithm across the 2^31 and 2^32 boundaries gives
+    the oracle's bits, and every counter advances by the call-number rule."""
+    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=TIMEOUT_US)
+    try:
+        _counters(ch, start)
+        sizes = [131_072, 10_240, 4096, 65_541, 9, 131_072]
+        for call, n in enumerate(sizes):
+            x0b, x1b = specials_mix(n, seed=700 + call), specials_mix(n, seed=800 + call)
+            x0, x1 = to_dev(x0b), to_dev(x1b)
+            out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+            say(f"exchange: counters from {start}, call {call}, n={n}, "
+                f"algorithm {ch.algorithm_for(n)}")
+            loopback(ch, x0, x1, out0, out1, streams)
+            check_pair(out0, out1, x0b, x1b, f"start {start} call {call} n={n}")
+        want = start
+        for _ in sizes:
+            want = _next_call_number(want)
+        assert _counters(ch) == [want] * (2 * ch.info().num_blocks)
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
