@@ -264,6 +264,7 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
     ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=5_000_000, world_size=world,
                     algorithm=algorithm)
     taken = ch.algorithm_for(n)
+    link_mbps = ch.info().link_mbps
     try:
         for _ in range(warmup):
             for r in range(world):
@@ -299,7 +300,7 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
         if taken == hr.HR_ALGO_LL:          # every 4 bytes of values travel with 4 of call number
             d2h, h2d = 2 * d2h, 2 * h2d
     return {
-        "world": world, "algorithm": ALGO_NAMES[taken],
+        "world": world, "algorithm": ALGO_NAMES[taken], "link_mbps": link_mbps,
         "tokens": tokens, "N": n, "bytes_per_call": alg,
         "graph_us": round(t_graph * 1e6, 3), "graph_GBps": round(alg / t_graph / 1e9, 2),
         "graph_frac_link": round(alg / t_graph / 1e9 / link_peak, 4),

@@ -95,6 +95,12 @@ typedef enum {
 /* Default watchdog for one wait on the peer, in microseconds. */
 #define HR_DEFAULT_TIMEOUT_US 1000000u
 
+/* Host-link rate the one-shot paces its workgroups by (MB/s; see
+   hr_channel_config.link_mbps): the default, and the value that turns pacing
+   off. */
+#define HR_DEFAULT_LINK_MBPS 55000u
+#define HR_LINK_UNPACED 0xFFFFFFFFu
+
 /* Exchange algorithm of a channel (all produce the same bits). */
 #define HR_ALGO_AUTO 0      /* two ranks: low-latency up to 10240 values,
                                one-shot above; 3+ ranks: one-shot, and
@@ -121,6 +127,19 @@ typedef struct {
                              compute units / world_size.                       */
     uint32_t timeout_us;  /* watchdog per wait; 0 = HR_DEFAULT_TIMEOUT_US      */
     int algorithm;        /* HR_ALGO_*; 0 = automatic                         */
+    uint32_t link_mbps;   /* rate (MB/s) of the host link that the channel's
+                             ranks share; 0 = HR_DEFAULT_LINK_MBPS (a PCIe 5.0
+                             x16 link as measured on MI355X hosts).  The
+                             one-shot starts workgroup b's publish b slices
+                             later than workgroup 0's, a slice taking
+                             world_size x slice bytes / link_mbps, so that
+                             each workgroup's flag and reads are not queued
+                             behind every other workgroup's writes (the link
+                             carries requests in order) and the reads of
+                             early slices overlap the writes of later ones.
+                             A rate above the real one only lets the writes
+                             queue again; one well below it delays the call.
+                             HR_LINK_UNPACED: no pacing.                      */
 } hr_channel_config;
 
 /* Read-only description of a channel, for diagnostics and tests. */
@@ -152,6 +171,8 @@ typedef struct {
                                      {v0v1, call, v2v3, call}, and word u of
                                      the second, {v4v5, call, v6v7, call}     */
     size_t ll_stride;             /* 16-byte words per low-latency slot       */
+    uint32_t link_mbps;           /* the pacing rate in effect (MB/s), or
+                                     HR_LINK_UNPACED                          */
     uint64_t *dev_epochs;         /* device address of the call counters
                                      [world][num_blocks]: the last call number
                                      each rank's workgroup took.  Call numbers

@@ -90,6 +90,7 @@ struct ExchArgs {
     uint32_t *host_error;     // device view of the host error word
     const uint32_t *abort_w;  // device view of the host abort word
     uint64_t timeout_ticks;
+    uint32_t pace_q16;        // wall-clock ticks per byte of a paced publish, x 2^16 (0: unpaced)
     int rank;
     int world;
     int nblocks;   // launched workgroups (the channel's fixed count)
@@ -193,6 +194,21 @@ __device__ __forceinline__ uint64_t next_call_number(uint64_t prev) {
     return static_cast<uint32_t>(e) == 0u ? e + 2u : e;
 }
 
+// Pacing of the publish: workgroup b starts b slices after workgroup 0 (the
+// ranks' workgroups b start together), a slice taking `slice_bytes` (one
+// workgroup's publish summed over the ranks that share the host link) at
+// the channel's link rate.  The link carries requests in order, so without
+// pacing every flag and every read request queues behind all of the call's
+// slot writes; paced, the queue stays short, each workgroup's handshake
+// completes early and the reads of early slices overlap the writes of later
+// ones.
+__device__ __forceinline__ void pace(const ExchArgs &a, int b, uint64_t slice_bytes) {
+    if (a.pace_q16 == 0 || b == 0) return;
+    const uint64_t wait = (static_cast<uint64_t>(b) * slice_bytes * a.pace_q16) >> 16;
+    const long long t0 = wall_clock64();
+    while (static_cast<uint64_t>(wall_clock64() - t0) < wait) __builtin_amdgcn_s_sleep(1);
+}
+
 // Advance this workgroup's call counter (every launched workgroup does, so a
 // rank's workgroups agree on the slot parity); returns the call number e, or
 // 0 when the channel already holds an error.
@@ -245,7 +261,9 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
     for (int q = 0; q < W; ++q)
         slot[q] = slot_rsrc(a.slots + static_cast<size_t>(W * parity + q) * a.stride, a.stride);
 
-    // 1. publish this rank's slice into its host slot (write-through)
+    // 1. publish this rank's slice into its host slot (write-through),
+    //    paced so that each workgroup's handshake and reads start early
+    pace(a, b, (hi - lo) * 16u * W);
     for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
         T x[kExchUnroll];
 #pragma unroll
@@ -366,7 +384,8 @@ __global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
         slot[q] = slot_rsrc(a.slots + static_cast<size_t>(W * parity + q) * a.stride, a.stride);
     const __amdgpu_buffer_rsrc_t red = slot_rsrc(a.reduced + static_cast<size_t>(parity) * a.stride, a.stride);
 
-    // A. publish
+    // A. publish (paced as the one-shot's)
+    pace(a, b, (hi - lo) * 16u * W);
     for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
         T x[kExchUnroll];
 #pragma unroll
@@ -712,6 +731,8 @@ struct hr_channel_s {
     int nblocks;
     uint32_t timeout_us;
     uint64_t timeout_ticks;
+    uint32_t link_mbps;        // pacing rate, or HR_LINK_UNPACED
+    uint32_t pace_q16;         // wall-clock ticks per byte x 2^16, 0 when unpaced
     void *host_base;           // hipHostMalloc'ed region (host address)
     unsigned char *host_dev;   // the same region as seen by the device
     int algorithm;             // HR_ALGO_*
@@ -788,6 +809,12 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->algorithm = cfg->algorithm;
     ch->timeout_us = timeout_us;
     ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
+    ch->link_mbps = cfg->link_mbps ? cfg->link_mbps : HR_DEFAULT_LINK_MBPS;
+    // ticks per byte = clock_khz * 1e3 / (link_mbps * 1e6)
+    ch->pace_q16 = ch->link_mbps == HR_LINK_UNPACED
+                       ? 0u
+                       : static_cast<uint32_t>((static_cast<uint64_t>(clock_khz) << 16) /
+                                               (static_cast<uint64_t>(ch->link_mbps) * 1000u));
 
     const size_t slot_bytes = 2 * static_cast<size_t>(world) * ch->stride * sizeof(uint16_t);
     const size_t flag_bytes = static_cast<size_t>(world) * static_cast<size_t>(nb) * kLine;
@@ -862,6 +889,7 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
     a.host_error = reinterpret_cast<uint32_t *>(ch->host_dev + ch->error_off);
     a.abort_w = reinterpret_cast<const uint32_t *>(ch->host_dev + ch->abort_off);
     a.timeout_ticks = ch->timeout_ticks;
+    a.pace_q16 = ch->pace_q16;
     a.rank = rank;
     a.world = ch->world_size;
     a.nblocks = ch->nblocks;
@@ -931,6 +959,7 @@ extern "C" HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *
     info->host_flags2 = reinterpret_cast<volatile uint64_t *>(base + ch->flags2_off);
     info->host_ll = base + ch->ll_off;
     info->dev_epochs = ch->dev_epochs;
+    info->link_mbps = ch->link_mbps;
     info->ll_stride = ch->ll_stride;
     return HR_OK;
 }

@@ -31,6 +31,8 @@ HR_MAX_WORLD = 8
 HR_DEFAULT_MAX_NUMEL = 131072
 HR_MAX_NUMEL_LIMIT = 1 << 29
 HR_DEFAULT_TIMEOUT_US = 1_000_000
+HR_DEFAULT_LINK_MBPS = 55_000
+HR_LINK_UNPACED = 0xFFFFFFFF
 HR_ALGO_AUTO = 0
 HR_ALGO_ONE_SHOT = 1
 HR_ALGO_TWO_SHOT = 2
@@ -60,7 +62,8 @@ class hr_channel_config(ctypes.Structure):
                 ("max_numel", ctypes.c_size_t),
                 ("num_blocks", ctypes.c_int),
                 ("timeout_us", ctypes.c_uint32),
-                ("algorithm", ctypes.c_int)]
+                ("algorithm", ctypes.c_int),
+                ("link_mbps", ctypes.c_uint32)]
 
 
 class hr_admit_policy(ctypes.Structure):
@@ -88,6 +91,7 @@ class hr_channel_info(ctypes.Structure):
                 ("host_flags2", ctypes.POINTER(ctypes.c_uint64)),
                 ("host_ll", ctypes.c_void_p),
                 ("ll_stride", ctypes.c_size_t),
+                ("link_mbps", ctypes.c_uint32),
                 ("dev_epochs", ctypes.c_void_p)]
 
 
@@ -145,9 +149,10 @@ def hr_status_str(status: int) -> str:
 
 
 def hr_create_channel(device: int = 0, world_size: int = 2, max_numel: int = 0,
-                      num_blocks: int = 0, timeout_us: int = 0, algorithm: int = 0) -> int:
+                      num_blocks: int = 0, timeout_us: int = 0, algorithm: int = 0,
+                      link_mbps: int = 0) -> int:
     """Returns the channel handle (an integer address) or raises HrError."""
-    cfg = hr_channel_config(device, world_size, max_numel, num_blocks, timeout_us, algorithm)
+    cfg = hr_channel_config(device, world_size, max_numel, num_blocks, timeout_us, algorithm, link_mbps)
     h = ctypes.c_void_p()
     st = load().hr_create_channel(ctypes.byref(cfg), ctypes.byref(h))
     if st != HR_OK:
@@ -298,10 +303,10 @@ class Channel:
     rank's call."""
 
     def __init__(self, device: int = 0, max_numel: int = 0, num_blocks: int = 0,
-                 timeout_us: int = 0, world_size: int = 2, algorithm: int = 0):
+                 timeout_us: int = 0, world_size: int = 2, algorithm: int = 0, link_mbps: int = 0):
         self.world_size = world_size
         self.handle = hr_create_channel(device, world_size, max_numel, num_blocks, timeout_us,
-                                        algorithm)
+                                        algorithm, link_mbps)
 
     def allreduce(self, rank: int, inp, out, stream=None):
         """One rank's call; torch.float16 or torch.bfloat16 tensors."""

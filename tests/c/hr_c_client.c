@@ -74,7 +74,8 @@ int main(int argc, char **argv)
 
     if (G == 2 && n <= HR_DEFAULT_MAX_NUMEL) {
         hr_channel ch = NULL;
-        hr_channel_config cfg = {0, 2, 0, 0, 2000000u, HR_ALGO_AUTO};
+        hr_channel_config cfg = {.device = 0, .world_size = 2, .timeout_us = 2000000u,
+                                 .algorithm = HR_ALGO_AUTO};
         CHECK_HR(hr_create_channel(&cfg, &ch));
         CHECK_HR(hr_loopback_stream_create(0, &s1));
         CHECK_HR(hr_allreduce_f16(ch, 0, dev[0], out[1], n, s0));

@@ -499,3 +499,25 @@ def test_call_numbers_far_from_zero(streams, start):
     finally:
         torch.cuda.synchronize()
         ch.destroy()
+
+
+@pytest.mark.parametrize("link_mbps", [hr.HR_LINK_UNPACED, 1000, 0], ids=["unpaced", "1GBps", "default"])
+@pytest.mark.parametrize("algorithm", [hr.HR_ALGO_ONE_SHOT, hr.HR_ALGO_TWO_SHOT], ids=["one-shot", "two-shot"])
+def test_publish_pacing(streams, link_mbps, algorithm):
+    """Paced or not, the one-shot and the two-shot give the oracle's bits.
+    At 1 GB/s the last workgroup of a 256 KiB call starts about half a
+    millisecond after the first; the watchdog does not mistake that for a
+    missing peer."""
+    ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=algorithm, link_mbps=link_mbps)
+    try:
+        want = hr.HR_DEFAULT_LINK_MBPS if link_mbps == 0 else link_mbps
+        assert ch.info().link_mbps == want
+        for call, n in enumerate([131_072, 65_541, 4096]):
+            x0b, x1b = specials_mix(n, seed=900 + call), specials_mix(n, seed=950 + call)
+            x0, x1 = to_dev(x0b), to_dev(x1b)
+            out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+            loopback(ch, x0, x1, out0, out1, streams)
+            check_pair(out0, out1, x0b, x1b, f"pacing {link_mbps} call {call} n={n}")
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
