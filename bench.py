@@ -316,6 +316,47 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
     }
 
 
+def exchange_prefill(c: Ctx, link_peak, sizes=(1 << 19, 1 << 23), calls=20):
+    """Two-rank calls far above the decode cap (1 and 16 MiB per rank), on a
+    channel made for them: paced one-shot (the automatic choice), the same
+    unpaced, and the two-shot."""
+    torch, hr, inputs = c.torch, c.hr, c.inputs
+    rows = []
+    for n in sizes:
+        xb = [inputs.gaussian(n, 0.5, 77, r) for r in range(2)]
+        x = [c.to_dev(b) for b in xb]
+        o = [torch.empty_like(t) for t in x]
+        ref = torch_fold(c, xb)
+        for algo, rate in ((hr.HR_ALGO_AUTO, 0), (hr.HR_ALGO_AUTO, hr.HR_LINK_UNPACED),
+                           (hr.HR_ALGO_TWO_SHOT, 0)):
+            ch = hr.Channel(max_numel=n, timeout_us=5_000_000, algorithm=algo, link_mbps=rate)
+            try:
+                for _ in range(3):
+                    for r in range(2):
+                        ch.allreduce(r, x[r], o[r], c.streams[r])
+                torch.cuda.synchronize()
+                graphs = [capture_calls(c, ch, r, x[r], o[r], c.streams[r], calls) for r in range(2)]
+                replay_pair(c, graphs, 20.0)
+                for t in o:
+                    t.zero_()
+                elapsed, _ = replay_pair(c, graphs, 20.0)
+                if ch.status() != hr.HR_OK:
+                    raise RuntimeError(f"exchange failed: {hr.hr_status_str(ch.status())}")
+                exact = all(same(c.np, c.to_host(t), ref) for t in o)
+                algo_name = ALGO_NAMES[ch.algorithm_for(n)]
+                del graphs
+                torch.cuda.synchronize()
+            finally:
+                ch.destroy()
+            t = elapsed / calls
+            alg = 3 * n * 2
+            rows.append({"N": n, "MiB_per_rank": n * 2 / 2**20, "algorithm": algo_name,
+                         "paced": rate != hr.HR_LINK_UNPACED, "graph_us": round(t * 1e6, 2),
+                         "graph_GBps": round(alg / t / 1e9, 2), "graph_frac_link": round(alg / t / 1e9 / link_peak, 4),
+                         "link_GBps_per_dir": round(2 * n * 2 / t / 1e9, 2), "bit_exact": exact})
+    return rows
+
+
 def workload5(c: Ctx, link_peak, algorithm=0, gate_ms=None):
     torch, hr, inputs = c.torch, c.hr, c.inputs
     calls = 1000
@@ -763,6 +804,8 @@ def main():
                         r.pop("_out")
                         rows.append(r)
             cfgs["exchange_world_host_slots"] = rows
+            log("exchange at prefill sizes (1 and 16 MiB per rank)")
+            cfgs["exchange_2rank_prefill"] = exchange_prefill(c, link_peak)
         if want("c5"):
             log("exchange graph of 1000 fresh calls, N=10240")
             cfgs["exchange_graph_1000_calls_N10240"] = workload5(c, link_peak, gate_ms=args.gate_ms)

@@ -521,3 +521,23 @@ def test_publish_pacing(streams, link_mbps, algorithm):
     finally:
         torch.cuda.synchronize()
         ch.destroy()
+
+
+@pytest.mark.parametrize("algorithm", [hr.HR_ALGO_AUTO, hr.HR_ALGO_TWO_SHOT], ids=["auto", "two-shot"])
+def test_prefill_sized_calls(streams, algorithm):
+    """Calls far above the 256 KiB decode cap (a channel made for them):
+    several 16-byte units per lane and long paced slices, ragged sizes,
+    every value checked against the oracle."""
+    n_max = 1 << 21                                    # 4 MiB per rank
+    ch = hr.Channel(max_numel=n_max, timeout_us=TIMEOUT_US, algorithm=algorithm)
+    try:
+        for call, n in enumerate([n_max, (1 << 20) + 3, 333_333, n_max - 7]):
+            x0b, x1b = inputs.gaussian(n, 0.5, 80, 0, call), inputs.gaussian(n, 0.5, 80, 1, call)
+            x0, x1 = to_dev(x0b), to_dev(x1b)
+            out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+            say(f"exchange: prefill-sized call {call}, n={n}, algorithm {ch.algorithm_for(n)}")
+            loopback(ch, x0, x1, out0, out1, streams)
+            check_pair(out0, out1, x0b, x1b, f"prefill call {call} n={n}")
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
