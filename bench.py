@@ -650,11 +650,20 @@ def cpu_model():
 
 # ---------------------------------------------------- counters (profiles/)
 
+def code_text(src):
+    """Source text without comments and with whitespace runs collapsed, so
+    that a digest of it changes only when the code does."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_digest():
+    """Digest of the kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     for f in ("fold.hip", "exchange.hip", "hr_internal.h"):
-        with open(os.path.join(ROOT, "message_fp16_all_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "message_fp16_all_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

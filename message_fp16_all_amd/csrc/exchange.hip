@@ -16,34 +16,44 @@
 // SGLang pull request "[SM120] Add optional FlashInfer PCIe-IPC all-reduce
 // for switch-free hosts", section "Accuracy", shows that order changes bits).
 //
+// Three algorithms, one channel, the same bits (a call takes one of them as
+// a function of the channel and numel, so every rank agrees): the one-shot
+// below (the source's method), the two-shot (exchange2_k) and the
+// low-latency one-shot for small calls (exchange_ll_k).
+//
 // Channel memory
 //   host (pinned, device-mapped, fine-grained/coherent):
 //     slots  [2 parity][W rank][stride] binary16 -- the 2 x world x numel
 //            workspace of the SGLang page's "Modifications" section
-//     flags  [W rank][nblocks], one 128-byte line each: the (64-bit) call
-//            number of the last chunk that workgroup published
+//     reduced-shard slots [2 parity][stride] (two-shot)
+//     flags, reduced-shard flags  [W rank][nblocks], one 128-byte line each:
+//            the 64-bit call number of the last slice that workgroup
+//            published
+//     low-latency slots [2 parity][W rank][2 halves][units] 16-byte words
 //     error word, abort word (one line each)
 //   device (HBM): epoch[W rank][nblocks] -- per-workgroup 64-bit call
-//     counter, device error word.
+//     counter (see next_call_number), device error word.
 //
 // Every launch has the channel's fixed workgroup count; each workgroup
 // advances its call counter, so parity is uniform across a call.  Only the
 // first `nactive` workgroups (a function of numel and W, so equal on every
-// rank)
-// carry values and take part in the flag handshake: fewer pollers means less
-// non-posted traffic on the host link, which is what bounds small calls.
+// rank) carry values and take part in the flag handshake: fewer pollers
+// means less non-posted traffic on the host link, which is what bounds
+// small calls.
 //
-// Call protocol of active workgroup b of rank r at call e (= its counter + 1):
+// One-shot protocol of active workgroup b of rank r at call e:
+//   0. wait b slices (pace): the link carries requests in order, and
+//      without pacing every flag and read would queue behind all writes
 //   1. load its slice of `in` and store it to slot[e & 1][r] with
 //      system-coherent (write-through) stores                        (D2H)
 //   2. every lane waits for its stores to be acknowledged; barrier; lane 0
 //      stores flag[r][b] = e at system scope -- the "fence, then flag" of
 //      the method, without a whole-cache write-back
 //   3. lanes q != r of the first wave poll flag[q][b] with system-scope
-//      loads until each reaches e (wrap-safe signed compare, so a peer
-//      already at e + 1 also releases the wait), sleeping between polls;
-//      lane 0 also polls the abort word, and a watchdog on the
-//      constant-rate wall clock bounds the wait
+//      loads until each reaches e (signed 64-bit compare, so a peer already
+//      at e + 1 also releases the wait), sleeping between polls; lane 0
+//      also polls the abort word, and a watchdog on the constant-rate wall
+//      clock bounds the wait
 //   4. barrier, then system-coherent loads of slot[e & 1][q] for every
 //      peer q (H2D) and plain loads of its own slice of `in` again; store
 //      the left fold x0 + x1 + ... + x_{W-1}, in rank order, to `out`.
