@@ -130,10 +130,11 @@ typedef struct {
     uint32_t link_mbps;   /* rate (MB/s) of the host link that the channel's
                              ranks share; 0 = HR_DEFAULT_LINK_MBPS (a PCIe 5.0
                              x16 link as measured on MI355X hosts).  The
-                             one-shot starts workgroup b's publish b slices
-                             later than workgroup 0's, a slice taking
-                             world_size x slice bytes / link_mbps, so that
-                             each workgroup's flag and reads are not queued
+                             one-shot and the two-shot start workgroup b's
+                             publish b - 2 slices later than workgroups
+                             0..2's, a slice taking world_size x slice bytes
+                             / link_mbps, so that each workgroup's flag and
+                             reads are not queued
                              behind every other workgroup's writes (the link
                              carries requests in order) and the reads of
                              early slices overlap the writes of later ones.

@@ -204,17 +204,21 @@ __device__ __forceinline__ uint64_t next_call_number(uint64_t prev) {
     return static_cast<uint32_t>(e) == 0u ? e + 2u : e;
 }
 
-// Pacing of the publish: workgroup b starts b slices after workgroup 0 (the
-// ranks' workgroups b start together), a slice taking `slice_bytes` (one
-// workgroup's publish summed over the ranks that share the host link) at
-// the channel's link rate.  The link carries requests in order, so without
-// pacing every flag and every read request queues behind all of the call's
-// slot writes; paced, the queue stays short, each workgroup's handshake
-// completes early and the reads of early slices overlap the writes of later
-// ones.
+// Pacing of the publish: workgroup b > kPaceBurst starts b - kPaceBurst
+// slices after the first ones (the ranks' workgroups b start together), a
+// slice taking `slice_bytes` (one workgroup's publish summed over the ranks
+// that share the host link) at the channel's link rate.  The link carries
+// requests in order, so without pacing every flag and every read request
+// queues behind all of the call's slot writes; paced, the queue stays
+// short, each workgroup's handshake completes early and the reads of early
+// slices overlap the writes of later ones.  The first kPaceBurst + 1
+// workgroups start together: the link is idle when a call starts, and
+// writes reach its rate only with a few slices in flight.
+constexpr int kPaceBurst = 2;
+
 __device__ __forceinline__ void pace(const ExchArgs &a, int b, uint64_t slice_bytes) {
-    if (a.pace_q16 == 0 || b == 0) return;
-    const uint64_t wait = (static_cast<uint64_t>(b) * slice_bytes * a.pace_q16) >> 16;
+    if (a.pace_q16 == 0 || b <= kPaceBurst) return;
+    const uint64_t wait = (static_cast<uint64_t>(b - kPaceBurst) * slice_bytes * a.pace_q16) >> 16;
     const long long t0 = wall_clock64();
     while (static_cast<uint64_t>(wall_clock64() - t0) < wait) __builtin_amdgcn_s_sleep(1);
 }
