@@ -306,7 +306,9 @@ HR_API hr_status hr_channel_status(hr_channel ch);
 /*
  * hr_channel_abort -- ask every kernel of this channel that is waiting, or
  * will wait, for its peer to stop: waits end with HR_ERR_ABORTED recorded in
- * the channel and `out` unwritten.  Host-side store only; returns at once.
+ * the channel and `out` unwritten.  A wait reads the abort word once it has
+ * lasted 20 us (polling it sooner slows every call), so a kernel stops within
+ * microseconds of that.  Host-side store only; returns at once.
  */
 HR_API hr_status hr_channel_abort(hr_channel ch);
 

@@ -51,9 +51,9 @@
 //      the method, without a whole-cache write-back
 //   3. lanes q != r of the first wave poll flag[q][b] with system-scope
 //      loads until each reaches e (signed 64-bit compare, so a peer already
-//      at e + 1 also releases the wait), sleeping between polls; lane 0
-//      also polls the abort word, and a watchdog on the constant-rate wall
-//      clock bounds the wait
+//      at e + 1 also releases the wait), sleeping between polls; a wait
+//      that lasts over 20 us also reads the abort word, and a watchdog on
+//      the constant-rate wall clock bounds the wait
 //   4. barrier, then system-coherent loads of slot[e & 1][q] for every
 //      peer q (H2D) and plain loads of its own slice of `in` again; store
 //      the left fold x0 + x1 + ... + x_{W-1}, in rank order, to `out`.
@@ -81,6 +81,7 @@ constexpr int kExchThreads = 256;
 constexpr int kExchUnroll = 4;                    // units per lane per publish batch
 constexpr int kMaxWorld = 8;
 constexpr int kMinActivePolls = 16;                // W * minimum active workgroups
+constexpr uint32_t kAbortAfterUs = 20;             // waits read the abort word only after this long
 constexpr size_t kLine = 128;                     // bytes per flag / word line
 constexpr size_t kFlagStride = kLine / sizeof(uint64_t);  // flags are 64-bit call numbers
 
@@ -100,6 +101,7 @@ struct ExchArgs {
     uint32_t *host_error;     // device view of the host error word
     const uint32_t *abort_w;  // device view of the host abort word
     uint64_t timeout_ticks;
+    uint64_t abort_after_ticks;  // waits shorter than this do not read the abort word
     uint32_t pace_q16;        // wall-clock ticks per byte of a paced publish, x 2^16 (0: unpaced)
     int rank;
     int world;
@@ -155,6 +157,19 @@ struct HostIO<uint16_t> {
     }
 };
 
+// True when a wait that has lasted `waited` ticks should end because the
+// host raised the abort word.  Waits shorter than abort_after_ticks do not
+// look: every waiting wave reading the same host line on every poll slows
+// the flags themselves (measured: 17.9 -> 22.7 us per 256 KiB call), and
+// flags normally arrive within microseconds.  Called by the whole wave; the
+// result is the same in every lane.
+__device__ __forceinline__ bool aborted(const ExchArgs &a, uint64_t waited) {
+    if (waited <= a.abort_after_ticks) return false;
+    uint32_t ab = 0;
+    if ((threadIdx.x % 64) == 0) ab = __hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return __shfl(ab, 0) != 0;
+}
+
 // Wait, in the first wave, until flag[q][b] >= e for every rank q whose bit
 // is set in `mask` (one lane per rank, wrap-safe compare), or the abort word
 // is set, or the watchdog expires.  Returns 0, HR_ERR_ABORTED or
@@ -174,14 +189,13 @@ __device__ __forceinline__ uint32_t wait_flags(const ExchArgs &a, const uint64_t
             done = static_cast<int64_t>(f - e) >= 0;
         }
         if (__all(done)) break;
-        uint32_t ab = 0;
-        if (lane == 0) ab = __hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        if (__shfl(ab, 0) != 0) {
-            status = HR_ERR_ABORTED;
+        const uint64_t waited = static_cast<uint64_t>(wall_clock64() - t0);
+        if (waited > a.timeout_ticks) {
+            status = HR_ERR_TIMEOUT;
             break;
         }
-        if (static_cast<uint64_t>(wall_clock64() - t0) > a.timeout_ticks) {
-            status = HR_ERR_TIMEOUT;
+        if (aborted(a, waited)) {
+            status = HR_ERR_ABORTED;
             break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -584,7 +598,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
     uint32_t status = 0;
     const long long t0 = wall_clock64();
     for (;;) {
-        // all pending peers' loads, and the abort word, in flight at once
+        // all pending peers' loads in flight at once
         u32x4 w0[W], w1[W];
 #pragma unroll
         for (int q = 0; q < W; ++q) {
@@ -593,8 +607,6 @@ __global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
                 w1[q] = __builtin_amdgcn_raw_buffer_load_b128(ll[q], off1, 0, kSysCoherent);
             }
         }
-        uint32_t ab = 0;
-        if (tid % 64 == 0) ab = __hip_atomic_load(a.abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 #pragma unroll
         for (int q = 0; q < W; ++q) {
             if (((pending >> q) & 1u) && w0[q].y == e && w0[q].w == e && w1[q].y == e && w1[q].w == e) {
@@ -603,12 +615,13 @@ __global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
             }
         }
         if (!__any(pending != 0u)) break;
-        if (__shfl(ab, 0) != 0) {
-            status = HR_ERR_ABORTED;
+        const uint64_t waited = static_cast<uint64_t>(wall_clock64() - t0);
+        if (waited > a.timeout_ticks) {
+            status = HR_ERR_TIMEOUT;
             break;
         }
-        if (static_cast<uint64_t>(wall_clock64() - t0) > a.timeout_ticks) {
-            status = HR_ERR_TIMEOUT;
+        if (aborted(a, waited)) {
+            status = HR_ERR_ABORTED;
             break;
         }
         __builtin_amdgcn_s_sleep(kLLSleep);
@@ -745,6 +758,7 @@ struct hr_channel_s {
     int nblocks;
     uint32_t timeout_us;
     uint64_t timeout_ticks;
+    uint64_t abort_after_ticks;
     uint32_t link_mbps;        // pacing rate, or HR_LINK_UNPACED
     uint32_t pace_q16;         // wall-clock ticks per byte x 2^16, 0 when unpaced
     void *host_base;           // hipHostMalloc'ed region (host address)
@@ -823,6 +837,7 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->algorithm = cfg->algorithm;
     ch->timeout_us = timeout_us;
     ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
+    ch->abort_after_ticks = static_cast<uint64_t>(kAbortAfterUs) * static_cast<uint64_t>(clock_khz) / 1000u;
     ch->link_mbps = cfg->link_mbps ? cfg->link_mbps : HR_DEFAULT_LINK_MBPS;
     // ticks per byte = clock_khz * 1e3 / (link_mbps * 1e6)
     ch->pace_q16 = ch->link_mbps == HR_LINK_UNPACED
@@ -903,6 +918,7 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
     a.host_error = reinterpret_cast<uint32_t *>(ch->host_dev + ch->error_off);
     a.abort_w = reinterpret_cast<const uint32_t *>(ch->host_dev + ch->abort_off);
     a.timeout_ticks = ch->timeout_ticks;
+    a.abort_after_ticks = ch->abort_after_ticks;
     a.pace_q16 = ch->pace_q16;
     a.rank = rank;
     a.world = ch->world_size;

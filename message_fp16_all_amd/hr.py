@@ -111,6 +111,13 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run python -m message_fp16_all_amd.build")
+    # torch ships its own HIP runtime under the same soname as the system one;
+    # whichever loads first serves the process.  Load torch's first (when
+    # torch is installed), so that the library and torch share one runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp = ctypes.c_void_p
     lib.hr_create_channel.argtypes = [ctypes.POINTER(hr_channel_config), ctypes.POINTER(vp)]
