@@ -100,6 +100,7 @@ typedef enum {
    off. */
 #define HR_DEFAULT_LINK_MBPS 55000u
 #define HR_LINK_UNPACED 0xFFFFFFFFu
+#define HR_MIN_LINK_MBPS 100u      /* smaller nonzero rates are refused */
 
 /* Exchange algorithm of a channel (all produce the same bits). */
 #define HR_ALGO_AUTO 0      /* two ranks: low-latency up to 10240 values,
@@ -197,7 +198,8 @@ typedef struct {
  * cfg:  see hr_channel_config.  *out receives the handle on success and is
  *       left untouched on failure.
  * Errors: HR_ERR_INVALID_ARG (null cfg/out, negative or out-of-range
- *       fields), HR_ERR_UNSUPPORTED (world_size outside 2..HR_MAX_WORLD),
+ *       fields, link_mbps below HR_MIN_LINK_MBPS), HR_ERR_UNSUPPORTED
+ *       (world_size outside 2..HR_MAX_WORLD),
  *       HR_ERR_HIP.
  */
 HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out);

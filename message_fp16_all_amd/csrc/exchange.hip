@@ -799,6 +799,7 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     if (cfg->world_size < 2 || cfg->world_size > kMaxWorld) return HR_ERR_UNSUPPORTED;
     if (cfg->device < 0 || cfg->num_blocks < 0) return HR_ERR_INVALID_ARG;
     if (cfg->algorithm < HR_ALGO_AUTO || cfg->algorithm > HR_ALGO_LL) return HR_ERR_INVALID_ARG;
+    if (cfg->link_mbps != 0 && cfg->link_mbps < HR_MIN_LINK_MBPS) return HR_ERR_INVALID_ARG;
     const size_t max_numel = cfg->max_numel ? cfg->max_numel : HR_DEFAULT_MAX_NUMEL;
     // A slot is addressed by a buffer descriptor whose byte count and
     // offsets are 32-bit: keep one slot at or below 1 GiB.
