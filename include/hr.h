@@ -103,7 +103,7 @@ typedef enum {
 #define HR_MIN_LINK_MBPS 100u      /* smaller nonzero rates are refused */
 
 /* Exchange algorithm of a channel (all produce the same bits). */
-#define HR_ALGO_AUTO 0      /* two ranks: low-latency up to 10240 values,
+#define HR_ALGO_AUTO 0      /* two ranks: low-latency up to 12288 values,
                                one-shot above; 3+ ranks: one-shot, and
                                two-shot from 32768 values                 */
 #define HR_ALGO_ONE_SHOT 1  /* every rank reads every peer's contribution */
@@ -211,7 +211,7 @@ HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out
  * for larger groups and payloads) instead has each shard's owner fold that
  * shard in rank order and publish it, and every rank gather the others'
  * folded shards: less host-link traffic for W > 2, the same bits.  The
- * low-latency one-shot (HR_ALGO_LL, or automatic for two ranks up to 10240
+ * low-latency one-shot (HR_ALGO_LL, or automatic for two ranks up to 12288
  * values) puts the call number into every 8-byte word it writes to host
  * memory, so a peer polls the values themselves: no flag, no wait for
  * acknowledgements, one host-link round trip less; the same bits again.

@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
 // stores nothing.  A word of an earlier use of the parity holds e - 2, never
 // e; parity safety is the one-shot's argument, with "flag" read as "word".
 constexpr size_t kLLMaxNumel = 32768;      // values per call the LL slots hold
-constexpr size_t kLLAutoMaxNumel = 10240;  // automatic choice takes LL up to here (20 KiB)
+constexpr size_t kLLAutoMaxNumel = 12288;  // automatic choice takes LL up to here (24 KiB)
 constexpr bool kLLAckFirst = true;         // first poll after the own words are acknowledged
 constexpr int kLLSleep = 8;                // s_sleep after a failed poll (x 64 clocks)
 

@@ -36,7 +36,7 @@ def streams():
     ls.destroy()
 
 
-# AUTO takes the low-latency one-shot up to 10240 values and the one-shot
+# AUTO takes the low-latency one-shot up to 12288 values and the one-shot
 # above; the two-shot is also correct for two ranks (each rank owns half of
 # the values), so the whole two-rank battery runs on every algorithm
 ALGOS = [hr.HR_ALGO_AUTO, hr.HR_ALGO_ONE_SHOT, hr.HR_ALGO_TWO_SHOT, hr.HR_ALGO_LL]
@@ -421,8 +421,8 @@ def test_algorithm_choice():
     chs = (ch2, ch2t, ch2l, ch4, ch4o)
     try:
         assert ch2.algorithm_for(1) == hr.HR_ALGO_LL
-        assert ch2.algorithm_for(10_240) == hr.HR_ALGO_LL
-        assert ch2.algorithm_for(10_241) == hr.HR_ALGO_ONE_SHOT
+        assert ch2.algorithm_for(12_288) == hr.HR_ALGO_LL
+        assert ch2.algorithm_for(12_289) == hr.HR_ALGO_ONE_SHOT
         assert ch2.algorithm_for(131_072) == hr.HR_ALGO_ONE_SHOT
         assert ch2t.algorithm_for(1) == hr.HR_ALGO_TWO_SHOT
         assert ch2l.algorithm_for(32_768) == hr.HR_ALGO_LL
