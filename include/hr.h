@@ -100,6 +100,7 @@ typedef enum {
    off. */
 #define HR_DEFAULT_LINK_MBPS 55000u
 #define HR_LINK_UNPACED 0xFFFFFFFFu
+#define HR_LINK_CALIBRATE 0xFFFFFFFEu /* measure the link at channel creation */
 #define HR_MIN_LINK_MBPS 100u      /* smaller nonzero rates are refused */
 
 /* Exchange algorithm of a channel (all produce the same bits). */
@@ -141,7 +142,12 @@ typedef struct {
                              early slices overlap the writes of later ones.
                              A rate above the real one only lets the writes
                              queue again; one well below it delays the call.
-                             HR_LINK_UNPACED: no pacing.                      */
+                             HR_LINK_UNPACED: no pacing.  HR_LINK_CALIBRATE:
+                             hr_create_channel times a 16 MiB pinned copy
+                             each way (best of 3, after a warm-up) and paces
+                             by the slower direction; this takes a few
+                             milliseconds and should run while the link is
+                             otherwise idle.                                  */
 } hr_channel_config;
 
 /* Read-only description of a channel, for diagnostics and tests. */

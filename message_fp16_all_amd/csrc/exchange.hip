@@ -786,6 +786,40 @@ struct DeviceGuard {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The host link's rate in MB/s, from pinned copies of kCalibBytes each way
+// on stream `s` (best of kCalibReps per direction, after one warm-up copy
+// each way): the slower direction, at least HR_MIN_LINK_MBPS; 0 when a HIP
+// call fails.
+uint32_t calibrate_link(hipStream_t s) {
+    constexpr size_t kCalibBytes = size_t(16) << 20;
+    constexpr int kCalibReps = 3;
+    void *host = nullptr, *dev = nullptr;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    float best[2] = {0.f, 0.f};  // ms per copy: host-to-device, device-to-host
+    bool ok = hipHostMalloc(&host, kCalibBytes, hipHostMallocDefault) == hipSuccess &&
+              hipMalloc(&dev, kCalibBytes) == hipSuccess && hipEventCreate(&ev[0]) == hipSuccess &&
+              hipEventCreate(&ev[1]) == hipSuccess;
+    for (int rep = -1; ok && rep < kCalibReps; ++rep) {
+        for (int dir = 0; ok && dir < 2; ++dir) {
+            ok = hipEventRecord(ev[0], s) == hipSuccess &&
+                 (dir == 0 ? hipMemcpyAsync(dev, host, kCalibBytes, hipMemcpyHostToDevice, s)
+                           : hipMemcpyAsync(host, dev, kCalibBytes, hipMemcpyDeviceToHost, s)) == hipSuccess &&
+                 hipEventRecord(ev[1], s) == hipSuccess && hipEventSynchronize(ev[1]) == hipSuccess;
+            float ms = 0.f;
+            ok = ok && hipEventElapsedTime(&ms, ev[0], ev[1]) == hipSuccess;
+            if (ok && rep >= 0 && ms > 0.f && (best[dir] == 0.f || ms < best[dir])) best[dir] = ms;
+        }
+    }
+    for (hipEvent_t e : ev)
+        if (e != nullptr) (void)hipEventDestroy(e);
+    if (dev != nullptr) (void)hipFree(dev);
+    if (host != nullptr) (void)hipHostFree(host);
+    if (!ok || best[0] <= 0.f || best[1] <= 0.f) return 0;
+    const double slower_ms = best[0] > best[1] ? best[0] : best[1];
+    const double mbps = static_cast<double>(kCalibBytes) / (slower_ms * 1e-3) / 1e6;
+    return mbps < HR_MIN_LINK_MBPS ? HR_MIN_LINK_MBPS : static_cast<uint32_t>(mbps);
+}
+
 void release(hr_channel ch) {
     if (ch->host_base) (void)hipHostFree(ch->host_base);
     if (ch->dev_base) (void)hipFree(ch->dev_base);
@@ -840,11 +874,6 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
     ch->abort_after_ticks = static_cast<uint64_t>(kAbortAfterUs) * static_cast<uint64_t>(clock_khz) / 1000u;
     ch->link_mbps = cfg->link_mbps ? cfg->link_mbps : HR_DEFAULT_LINK_MBPS;
-    // ticks per byte = clock_khz * 1e3 / (link_mbps * 1e6)
-    ch->pace_q16 = ch->link_mbps == HR_LINK_UNPACED
-                       ? 0u
-                       : static_cast<uint32_t>((static_cast<uint64_t>(clock_khz) << 16) /
-                                               (static_cast<uint64_t>(ch->link_mbps) * 1000u));
 
     const size_t slot_bytes = 2 * static_cast<size_t>(world) * ch->stride * sizeof(uint16_t);
     const size_t flag_bytes = static_cast<size_t>(world) * static_cast<size_t>(nb) * kLine;
@@ -871,11 +900,20 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
               hipStreamCreateWithFlags(&init, hipStreamNonBlocking) == hipSuccess &&
               hipMemsetAsync(ch->dev_base, 0, word_bytes, init) == hipSuccess &&
               hipStreamSynchronize(init) == hipSuccess;
+    if (ok && ch->link_mbps == HR_LINK_CALIBRATE) {
+        ch->link_mbps = calibrate_link(init);
+        ok = ch->link_mbps != 0;
+    }
     if (init != nullptr) (void)hipStreamDestroy(init);
     if (!ok) {
         release(ch);
         return HR_ERR_HIP;
     }
+    // ticks per byte = clock_khz * 1e3 / (link_mbps * 1e6)
+    ch->pace_q16 = ch->link_mbps == HR_LINK_UNPACED
+                       ? 0u
+                       : static_cast<uint32_t>((static_cast<uint64_t>(clock_khz) << 16) /
+                                               (static_cast<uint64_t>(ch->link_mbps) * 1000u));
     ch->host_dev = static_cast<unsigned char *>(dev_view);
     ch->dev_epochs = static_cast<uint64_t *>(ch->dev_base);
     ch->dev_error = reinterpret_cast<uint32_t *>(ch->dev_epochs + static_cast<size_t>(world) * nb);

@@ -33,6 +33,7 @@ HR_MAX_NUMEL_LIMIT = 1 << 29
 HR_DEFAULT_TIMEOUT_US = 1_000_000
 HR_DEFAULT_LINK_MBPS = 55_000
 HR_LINK_UNPACED = 0xFFFFFFFF
+HR_LINK_CALIBRATE = 0xFFFFFFFE
 HR_MIN_LINK_MBPS = 100
 HR_ALGO_AUTO = 0
 HR_ALGO_ONE_SHOT = 1

@@ -501,7 +501,8 @@ def test_call_numbers_far_from_zero(streams, start):
         ch.destroy()
 
 
-@pytest.mark.parametrize("link_mbps", [hr.HR_LINK_UNPACED, 1000, 0], ids=["unpaced", "1GBps", "default"])
+@pytest.mark.parametrize("link_mbps", [hr.HR_LINK_UNPACED, 1000, 0, hr.HR_LINK_CALIBRATE],
+                         ids=["unpaced", "1GBps", "default", "calibrated"])
 @pytest.mark.parametrize("algorithm", [hr.HR_ALGO_ONE_SHOT, hr.HR_ALGO_TWO_SHOT], ids=["one-shot", "two-shot"])
 def test_publish_pacing(streams, link_mbps, algorithm):
     """Paced or not, the one-shot and the two-shot give the oracle's bits.
@@ -510,8 +511,13 @@ def test_publish_pacing(streams, link_mbps, algorithm):
     missing peer."""
     ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=algorithm, link_mbps=link_mbps)
     try:
-        want = hr.HR_DEFAULT_LINK_MBPS if link_mbps == 0 else link_mbps
-        assert ch.info().link_mbps == want
+        got = ch.info().link_mbps
+        if link_mbps == hr.HR_LINK_CALIBRATE:
+            # a PCIe 5.0 x16 host link moves about 50-60 GB/s each way
+            say(f"calibrated host link: {got} MB/s")
+            assert 20_000 <= got <= 80_000
+        else:
+            assert got == (hr.HR_DEFAULT_LINK_MBPS if link_mbps == 0 else link_mbps)
         for call, n in enumerate([131_072, 65_541, 4096]):
             x0b, x1b = specials_mix(n, seed=900 + call), specials_mix(n, seed=950 + call)
             x0, x1 = to_dev(x0b), to_dev(x1b)
