@@ -95,9 +95,9 @@ typedef enum {
 /* Default watchdog for one wait on the peer, in microseconds. */
 #define HR_DEFAULT_TIMEOUT_US 1000000u
 
-/* Host-link rate the one-shot paces its workgroups by (MB/s; see
-   hr_channel_config.link_mbps): the default, and the value that turns pacing
-   off. */
+/* Host-link rate the one-shot and the two-shot pace their workgroups by
+   (MB/s; see hr_channel_config.link_mbps): the default, the values that turn
+   pacing off and that measure the link, and the smallest rate accepted. */
 #define HR_DEFAULT_LINK_MBPS 55000u
 #define HR_LINK_UNPACED 0xFFFFFFFFu
 #define HR_LINK_CALIBRATE 0xFFFFFFFEu /* measure the link at channel creation */
@@ -136,10 +136,10 @@ typedef struct {
                              publish b - 2 slices later than workgroups
                              0..2's, a slice taking world_size x slice bytes
                              / link_mbps, so that each workgroup's flag and
-                             reads are not queued
-                             behind every other workgroup's writes (the link
-                             carries requests in order) and the reads of
-                             early slices overlap the writes of later ones.
+                             reads are not queued behind every other
+                             workgroup's writes (the link carries requests in
+                             order) and the reads of early slices overlap
+                             the writes of later ones.
                              A rate above the real one only lets the writes
                              queue again; one well below it delays the call.
                              HR_LINK_UNPACED: no pacing.  HR_LINK_CALIBRATE:
@@ -205,8 +205,8 @@ typedef struct {
  *       left untouched on failure.
  * Errors: HR_ERR_INVALID_ARG (null cfg/out, negative or out-of-range
  *       fields, link_mbps below HR_MIN_LINK_MBPS), HR_ERR_UNSUPPORTED
- *       (world_size outside 2..HR_MAX_WORLD),
- *       HR_ERR_HIP.
+ *       (world_size outside 2..HR_MAX_WORLD), HR_ERR_HIP (including a failed
+ *       link measurement under HR_LINK_CALIBRATE).
  */
 HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out);
 
@@ -224,8 +224,8 @@ HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out
  *
  * Enqueues exactly one kernel on `stream`.  Its workgroups each own one
  * contiguous slice of the numel values: they copy the slice of `in` into this
- * rank's host slot of the current parity, make the stores visible at system
- * scope, raise their ready flag, wait (watchdog-bounded) for every peer's
+ * rank's host slot of the current parity (paced at the channel's link rate),
+ * make the stores visible at system scope, raise their ready flag, wait (watchdog-bounded) for every peer's
  * flag of the same call, read the peers' slices from their host slots and
  * write the left fold x0 + x1 + ... in rank order, one binary16 rounding per
  * add, to `out` (for two ranks fl16(x0 + x1), the 1Cat-vLLM page's
@@ -325,8 +325,10 @@ HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *info);
 
 /*
  * hr_destroy -- release the channel.  Destroy any graph that captured calls
- * on it first, then synchronise both rank streams, then call this; it
- * synchronises the channel's device before freeing.  NULL is a no-op.
+ * on it first, then synchronise the rank streams, then call this.  It
+ * synchronises the channel's whole device before freeing the host memory the
+ * kernels use, so it also waits for other work there (another channel's
+ * waits end at the latest at that channel's watchdog).  NULL is a no-op.
  */
 HR_API hr_status hr_destroy(hr_channel ch);
 
@@ -334,10 +336,10 @@ HR_API hr_status hr_destroy(hr_channel ch);
  * hr_loopback_stream_create -- a stream for one rank of a loopback channel.
  *
  * The launches of one exchange call (one per rank) must run at the same
- * time.  The HIP
- * runtime spreads ordinary streams over a small pool of hardware queues
- * (GPU_MAX_HW_QUEUES), and two streams that share a queue run their kernels
- * one after the other, so ordinary streams give no such guarantee.  A stream
+ * time.  The HIP runtime spreads ordinary streams over a small pool of
+ * hardware queues (GPU_MAX_HW_QUEUES), and two streams that share a queue run
+ * their kernels one after the other, so ordinary streams give no such
+ * guarantee.  A stream
  * created here owns its hardware queue: it is created with an explicit
  * compute-unit mask (the runtime never pools such queues) that enables every
  * compute unit of `device`.  It is ordered with the null stream like any
