@@ -283,11 +283,19 @@ def _f16_ptr(t, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
-def _stream_handle(stream) -> int:
+def _stream_handle(stream, tensor=None) -> int:
+    """The hipStream_t of ``stream``; for None, torch's current stream on the
+    device of ``tensor`` (or the current device).  torch's raw query returns
+    the handle without building a Stream object, which costs more than the
+    library call itself; the public call is the fallback."""
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return int(stream.cuda_stream)
+    if stream is not None:
+        return int(stream.cuda_stream)
+    dev = tensor.get_device() if tensor is not None else torch.cuda.current_device()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(dev))
+    return int(torch.cuda.current_stream(dev).cuda_stream)
 
 
 def reduce(tensors, out, stream=None):
@@ -303,7 +311,7 @@ def reduce(tensors, out, stream=None):
             raise ValueError(f"tensors[{i}] has {t.numel()} values, out has {n}")
         ptrs.append(_f16_ptr(t, f"tensors[{i}]", dt))
     fn, name = (hr_reduce_bf16, "hr_reduce_bf16") if bf else (hr_reduce_f16, "hr_reduce_f16")
-    _check(fn(ptrs, len(ptrs), _f16_ptr(out, "out", dt), n, _stream_handle(stream)), name)
+    _check(fn(ptrs, len(ptrs), _f16_ptr(out, "out", dt), n, _stream_handle(stream, out)), name)
     return out
 
 
@@ -327,7 +335,7 @@ class Channel:
         dt = torch.bfloat16 if bf else torch.float16
         fn, name = (hr_allreduce_bf16, "hr_allreduce_bf16") if bf else (hr_allreduce_f16, "hr_allreduce_f16")
         _check(fn(self.handle, rank, _f16_ptr(inp, "in", dt), _f16_ptr(out, "out", dt), n,
-                  _stream_handle(stream)), name)
+                  _stream_handle(stream, out)), name)
         return out
 
     def status(self) -> int:

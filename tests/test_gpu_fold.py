@@ -182,3 +182,14 @@ def test_contributions_in_the_workspace_layout(G, n):
     hr.reduce(views, views[0])
     torch.cuda.synchronize()
     assert_same_bits(to_host(views[0]), ref, f"workspace in place G={G} n={n}")
+
+
+def test_binding_takes_torchs_current_stream():
+    """With no stream given, the binding enqueues on torch's current stream,
+    also inside a stream context."""
+    t = torch.zeros(8, dtype=torch.float16, device="cuda:0")
+    assert hr._stream_handle(None, t) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert hr._stream_handle(None, t) == s.cuda_stream
+        assert hr._stream_handle(None) == s.cuda_stream
