@@ -90,3 +90,47 @@ def test_random_fold_sequence():
         torch.cuda.synchronize()
         ref = oracle.fold_bf16(xb) if bf16 else oracle.fold(xb)
         assert_same_bits(to_host(out), ref, f"fold {call}", bf16=bf16)
+
+
+def test_low_latency_graph_replayed_with_fresh_inputs():
+    """10 replays of a 1000-call low-latency graph per rank (N = 10240, the
+    decode workload), fresh inputs before every replay: every one of the
+    20000 outputs is compared with the oracle.  Guards the low-latency
+    protocol's reliance on whole 8-byte words over many calls."""
+    calls, n, replays = 1000, 10_240, 10
+    streams = hr.LoopbackStreams(0)
+    ch = hr.Channel(timeout_us=2_000_000, algorithm=hr.HR_ALGO_LL)
+    try:
+        assert ch.algorithm_for(n) == hr.HR_ALGO_LL
+        xin = [torch.empty((calls, n), dtype=torch.float16, device="cuda:0") for _ in range(2)]
+        outs = [torch.empty_like(x) for x in xin]
+        ch.allreduce(0, xin[0][0], outs[0][0], streams[0])
+        ch.allreduce(1, xin[1][0], outs[1][0], streams[1])
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=streams[r]):
+                for k in range(calls):
+                    ch.allreduce(r, xin[r][k], outs[r][k], streams[r])
+            graphs.append(g)
+        rng = np.random.default_rng(5)
+        for rep in range(replays):
+            xb = [rng.standard_normal((calls, n), dtype=np.float32).astype(np.float16).view(np.uint16)
+                  for _ in range(2)]
+            for r in range(2):
+                xin[r].copy_(to_dev(xb[r].reshape(-1)).view(calls, n))
+            torch.cuda.synchronize()
+            for r in range(2):
+                with torch.cuda.stream(streams[r]):
+                    graphs[r].replay()
+            for s in streams:
+                s.synchronize()
+            assert ch.status() == hr.HR_OK
+            ref = oracle.add(xb[0].reshape(-1), xb[1].reshape(-1))
+            for r in range(2):
+                assert_same_bits(to_host(outs[r]).reshape(-1), ref, f"replay {rep} rank {r}")
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+        streams.destroy()
