@@ -865,6 +865,8 @@ def main():
         "roofline": {"bound": "host-link", "achieved": round(achieved, 3), "peak": link_peak,
                      "unit": "GB/s", "frac": round(achieved / link_peak, 4),
                      "traffic": measured_traffic("exchange_k<2,true,F16>"),
+                     "traffic_unit": "bytes per rank launch: FETCH_SIZE (scaled by a plain copy) "
+                                     "+ WRITE_SIZE, HBM and host bytes together",
                      "kernel": "hr::exchange_k<2, true, hr::F16>",
                      "peak_source": "pinned hipMemcpyAsync probe, max(H2D, D2H) at 64 MiB, this run",
                      "link_GBps_per_dir": head["link_GBps_per_dir"]},
@@ -885,6 +887,7 @@ def main():
             "separate_allocations_frac": f4["cold_frac_hbm"], "warm_frac": f4["warm_frac_hbm"],
             "single_launch_frac": f4["cold_single_frac_hbm"],
             "traffic": measured_traffic("fold_vec<8,4,F16>"),
+            "traffic_unit": "bytes per launch: FETCH_SIZE (scaled by a plain copy) + WRITE_SIZE",
         }
     if cpu is not None:
         line["cpu_baseline"] = {
