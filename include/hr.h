@@ -98,7 +98,7 @@ typedef enum {
 /* Host-link rate the one-shot and the two-shot pace their workgroups by
    (MB/s; see hr_channel_config.link_mbps): the default, the values that turn
    pacing off and that measure the link, and the smallest rate accepted. */
-#define HR_DEFAULT_LINK_MBPS 55000u
+#define HR_DEFAULT_LINK_MBPS 50000u
 #define HR_LINK_UNPACED 0xFFFFFFFFu
 #define HR_LINK_CALIBRATE 0xFFFFFFFEu /* measure the link at channel creation */
 #define HR_MIN_LINK_MBPS 100u      /* smaller nonzero rates are refused */
@@ -129,9 +129,12 @@ typedef struct {
                              compute units / world_size.                       */
     uint32_t timeout_us;  /* watchdog per wait; 0 = HR_DEFAULT_TIMEOUT_US      */
     int algorithm;        /* HR_ALGO_*; 0 = automatic                         */
-    uint32_t link_mbps;   /* rate (MB/s) of the host link that the channel's
-                             ranks share; 0 = HR_DEFAULT_LINK_MBPS (a PCIe 5.0
-                             x16 link as measured on MI355X hosts).  The
+    uint32_t link_mbps;   /* rate (MB/s) at which the host link that the
+                             channel's ranks share carries writes while
+                             reads run the other way; 0 =
+                             HR_DEFAULT_LINK_MBPS (a PCIe 5.0 x16 link as
+                             measured on MI355X hosts, whose one-way copies
+                             reach 55 GB/s).  The
                              one-shot and the two-shot start workgroup b's
                              publish b - 2 slices later than workgroups
                              0..2's, a slice taking world_size x slice bytes
@@ -143,9 +146,10 @@ typedef struct {
                              A rate above the real one only lets the writes
                              queue again; one well below it delays the call.
                              HR_LINK_UNPACED: no pacing.  HR_LINK_CALIBRATE:
-                             hr_create_channel times a 16 MiB pinned copy
-                             each way (best of 3, after a warm-up) and paces
-                             by the slower direction; this takes a few
+                             hr_create_channel times a kernel that writes
+                             16 MiB to pinned host memory while it reads
+                             16 MiB from it (best of 3, after a warm-up) and
+                             paces by that rate; this takes a few
                              milliseconds and should run while the link is
                              otherwise idle.                                  */
 } hr_channel_config;

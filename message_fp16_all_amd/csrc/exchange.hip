@@ -114,11 +114,11 @@ __device__ __forceinline__ u32x4 combine(u32x4 x0, u32x4 x1) { return E::add8(x0
 template <class E>
 __device__ __forceinline__ uint16_t combine(uint16_t x0, uint16_t x1) { return E::add1(x0, x1); }
 
-// Units per lane per combine batch: W loads each, at most 8 in flight.
-template <int W>
-struct CombineShape {
-    static constexpr int U = (8 / W) > 0 ? (8 / W) : 1;
-};
+// The combine takes one 16-byte unit per lane per step (W loads in flight
+// per lane).  Reads of host memory lose rate when too many are in flight at
+// once: measured on MI355X with two ranks, 16 MiB per rank, four units per
+// lane per step took 805 us per call and one unit 781 us; 256 KiB calls (one
+// unit per lane in all) are unchanged.
 
 // Host-slot accesses are buffer loads/stores with the system-coherence bits
 // (sc0 sc1): stores write through every GPU cache level to host memory and
@@ -327,27 +327,14 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
     if (s_status != 0) return;
 
     // 4. combine: left fold in rank order x0 + x1 + ... + x_{W-1}
-    constexpr int UC = CombineShape<W>::U;
-    for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * UC) {
-        T x[W][UC];
+    for (size_t v = ulo + tid; v < uhi; v += kExchThreads) {
+        T x[W];
 #pragma unroll
-        for (int u = 0; u < UC; ++u) {
-            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < uhi) {
+        for (int q = 0; q < W; ++q) x[q] = (q == rank) ? in[v] : HostIO<T>::load(slot[q], v);
+        T acc = x[0];
 #pragma unroll
-                for (int q = 0; q < W; ++q) x[q][u] = (q == rank) ? in[v] : HostIO<T>::load(slot[q], v);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < UC; ++u) {
-            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < uhi) {
-                T acc = x[0][u];
-#pragma unroll
-                for (int q = 1; q < W; ++q) acc = combine<E>(acc, x[q][u]);
-                out[v] = acc;
-            }
-        }
+        for (int q = 1; q < W; ++q) acc = combine<E>(acc, x[q]);
+        out[v] = acc;
     }
     if (last && tail0 + tid < a.numel) {
         const size_t i = tail0 + tid;
@@ -443,28 +430,15 @@ __global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
         }
         __syncthreads();
         if (s_status != 0) return;
-        constexpr int UC = CombineShape<W>::U;
-        for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * UC) {
-            T x[W][UC];
+        for (size_t v = ulo + tid; v < uhi; v += kExchThreads) {
+            T x[W];
 #pragma unroll
-            for (int u = 0; u < UC; ++u) {
-                const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-                if (v < uhi) {
+            for (int q = 0; q < W; ++q) x[q] = (q == rank) ? in[v] : HostIO<T>::load(slot[q], v);
+            T acc = x[0];
 #pragma unroll
-                    for (int q = 0; q < W; ++q) x[q][u] = (q == rank) ? in[v] : HostIO<T>::load(slot[q], v);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < UC; ++u) {
-                const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-                if (v < uhi) {
-                    T acc = x[0][u];
-#pragma unroll
-                    for (int q = 1; q < W; ++q) acc = combine<E>(acc, x[q][u]);
-                    out[v] = acc;
-                    HostIO<T>::store(red, v, acc);
-                }
-            }
+            for (int q = 1; q < W; ++q) acc = combine<E>(acc, x[q]);
+            out[v] = acc;
+            HostIO<T>::store(red, v, acc);
         }
         if (last && tail0 + tid < a.numel) {
             const size_t i = tail0 + tid;
@@ -650,6 +624,40 @@ __global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
     }
 }
 
+// Link calibration: workgroups [0, nw) store `units` 16-byte units of `src`
+// to the host buffer `hw` while workgroups [nw, nw + nr) load `units` units
+// of the host buffer `hrd` (four loads per lane in flight), which is how an
+// exchange's publish and combine share the link; `sink` keeps the loads.
+constexpr int kCalibReadUnroll = 4;
+
+__global__ __launch_bounds__(kExchThreads) void link_probe_k(const u32x4 *src, u32x4 *hw, const u32x4 *hrd,
+                                                             u32x4 *sink, int units, int nw, int nr) {
+    const int b = blockIdx.x;
+    const int tid = static_cast<int>(threadIdx.x);
+    if (b < nw) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(hw, 0, units * 16, kRawBufferDword3);
+        for (int u = b * kExchThreads + tid; u < units; u += nw * kExchThreads)
+            __builtin_amdgcn_raw_buffer_store_b128(src[u], r, u * 16, 0, kSysCoherent);
+        return;
+    }
+    const int rb = b - nw;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(hrd), 0, units * 16, kRawBufferDword3);
+    const int step = nr * kExchThreads;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int u0 = rb * kExchThreads + tid; u0 < units; u0 += step * kCalibReadUnroll) {
+        u32x4 x[kCalibReadUnroll];
+#pragma unroll
+        for (int l = 0; l < kCalibReadUnroll; ++l) {
+            const int u = u0 + l * step;
+            x[l] = u < units ? __builtin_amdgcn_raw_buffer_load_b128(r, u * 16, 0, kSysCoherent) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int l = 0; l < kCalibReadUnroll; ++l) acc ^= x[l];
+    }
+    sink[rb * kExchThreads + tid] = acc;
+}
+
 // Active workgroups of an LL call: one unit per lane.
 inline int active_blocks_ll(size_t numel) {
     const size_t nunits = (numel + kVecElems - 1) / kVecElems;
@@ -786,37 +794,50 @@ struct DeviceGuard {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// The host link's rate in MB/s, from pinned copies of kCalibBytes each way
-// on stream `s` (best of kCalibReps per direction, after one warm-up copy
-// each way): the slower direction, at least HR_MIN_LINK_MBPS; 0 when a HIP
-// call fails.
-uint32_t calibrate_link(hipStream_t s) {
+// The rate (MB/s) at which the host link carries writes while reads run the
+// other way, which is what a paced exchange's publish meets: link_probe_k
+// moves kCalibBytes each way at once on stream `s` (best of kCalibReps after
+// one warm-up), with writers and readers in the proportion that moved the
+// most in a sweep on MI355X (128 and 64 workgroups).  At least
+// HR_MIN_LINK_MBPS; 0 when a HIP call fails.
+uint32_t calibrate_link(hipStream_t s, int cus) {
     constexpr size_t kCalibBytes = size_t(16) << 20;
     constexpr int kCalibReps = 3;
-    void *host = nullptr, *dev = nullptr;
+    const int units = static_cast<int>(kCalibBytes / sizeof(u32x4));
+    int nw = cus / 2 < 128 ? cus / 2 : 128, nr = cus / 4 < 64 ? cus / 4 : 64;
+    if (nw < 1) nw = 1;
+    if (nr < 1) nr = 1;
+    void *hw = nullptr, *hrd = nullptr, *dhw = nullptr, *dhr = nullptr, *src = nullptr, *sink = nullptr;
     hipEvent_t ev[2] = {nullptr, nullptr};
-    float best[2] = {0.f, 0.f};  // ms per copy: host-to-device, device-to-host
-    bool ok = hipHostMalloc(&host, kCalibBytes, hipHostMallocDefault) == hipSuccess &&
-              hipMalloc(&dev, kCalibBytes) == hipSuccess && hipEventCreate(&ev[0]) == hipSuccess &&
+    float best = 0.f;
+    bool ok = hipHostMalloc(&hw, kCalibBytes, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
+              hipHostMalloc(&hrd, kCalibBytes, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
+              hipHostGetDevicePointer(&dhw, hw, 0) == hipSuccess &&
+              hipHostGetDevicePointer(&dhr, hrd, 0) == hipSuccess && hipMalloc(&src, kCalibBytes) == hipSuccess &&
+              hipMalloc(&sink, static_cast<size_t>(nr) * kExchThreads * sizeof(u32x4)) == hipSuccess &&
+              hipMemsetAsync(src, 0, kCalibBytes, s) == hipSuccess && hipEventCreate(&ev[0]) == hipSuccess &&
               hipEventCreate(&ev[1]) == hipSuccess;
     for (int rep = -1; ok && rep < kCalibReps; ++rep) {
-        for (int dir = 0; ok && dir < 2; ++dir) {
-            ok = hipEventRecord(ev[0], s) == hipSuccess &&
-                 (dir == 0 ? hipMemcpyAsync(dev, host, kCalibBytes, hipMemcpyHostToDevice, s)
-                           : hipMemcpyAsync(host, dev, kCalibBytes, hipMemcpyDeviceToHost, s)) == hipSuccess &&
-                 hipEventRecord(ev[1], s) == hipSuccess && hipEventSynchronize(ev[1]) == hipSuccess;
-            float ms = 0.f;
-            ok = ok && hipEventElapsedTime(&ms, ev[0], ev[1]) == hipSuccess;
-            if (ok && rep >= 0 && ms > 0.f && (best[dir] == 0.f || ms < best[dir])) best[dir] = ms;
+        ok = hipEventRecord(ev[0], s) == hipSuccess;
+        if (ok) {
+            hipLaunchKernelGGL(link_probe_k, dim3(nw + nr), dim3(kExchThreads), 0, s, static_cast<const u32x4 *>(src),
+                               static_cast<u32x4 *>(dhw), static_cast<const u32x4 *>(dhr), static_cast<u32x4 *>(sink),
+                               units, nw, nr);
+            ok = hipGetLastError() == hipSuccess && hipEventRecord(ev[1], s) == hipSuccess &&
+                 hipEventSynchronize(ev[1]) == hipSuccess;
         }
+        float ms = 0.f;
+        ok = ok && hipEventElapsedTime(&ms, ev[0], ev[1]) == hipSuccess;
+        if (ok && rep >= 0 && ms > 0.f && (best == 0.f || ms < best)) best = ms;
     }
     for (hipEvent_t e : ev)
         if (e != nullptr) (void)hipEventDestroy(e);
-    if (dev != nullptr) (void)hipFree(dev);
-    if (host != nullptr) (void)hipHostFree(host);
-    if (!ok || best[0] <= 0.f || best[1] <= 0.f) return 0;
-    const double slower_ms = best[0] > best[1] ? best[0] : best[1];
-    const double mbps = static_cast<double>(kCalibBytes) / (slower_ms * 1e-3) / 1e6;
+    if (sink != nullptr) (void)hipFree(sink);
+    if (src != nullptr) (void)hipFree(src);
+    if (hrd != nullptr) (void)hipHostFree(hrd);
+    if (hw != nullptr) (void)hipHostFree(hw);
+    if (!ok || best <= 0.f) return 0;
+    const double mbps = static_cast<double>(kCalibBytes) / (static_cast<double>(best) * 1e-3) / 1e6;
     return mbps < HR_MIN_LINK_MBPS ? HR_MIN_LINK_MBPS : static_cast<uint32_t>(mbps);
 }
 
@@ -901,7 +922,7 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
               hipMemsetAsync(ch->dev_base, 0, word_bytes, init) == hipSuccess &&
               hipStreamSynchronize(init) == hipSuccess;
     if (ok && ch->link_mbps == HR_LINK_CALIBRATE) {
-        ch->link_mbps = calibrate_link(init);
+        ch->link_mbps = calibrate_link(init, cus);
         ok = ch->link_mbps != 0;
     }
     if (init != nullptr) (void)hipStreamDestroy(init);

@@ -31,7 +31,7 @@ HR_MAX_WORLD = 8
 HR_DEFAULT_MAX_NUMEL = 131072
 HR_MAX_NUMEL_LIMIT = 1 << 29
 HR_DEFAULT_TIMEOUT_US = 1_000_000
-HR_DEFAULT_LINK_MBPS = 55_000
+HR_DEFAULT_LINK_MBPS = 50_000
 HR_LINK_UNPACED = 0xFFFFFFFF
 HR_LINK_CALIBRATE = 0xFFFFFFFE
 HR_MIN_LINK_MBPS = 100
