@@ -253,6 +253,37 @@ __device__ __forceinline__ uint64_t next_call(const ExchArgs &a, int b) {
     return s_epoch;
 }
 
+// Loads and stores share one counter on this GPU (vmcnt), and the compiler
+// cannot wait for a load with a partial count once a store is outstanding
+// too, so in these bounds-checked batch loops each host store waits for the
+// one before it: a lane has one publish store in flight at a time.  Letting
+// a batch's stores go out together (one explicit wait after its loads) was
+// measured slower on MI355X for calls of several batches per lane (4 MiB
+// per rank, two ranks: 183.6 -> 186.2 us; four ranks, 2 MiB: 313 -> 321
+// us): with pacing in place, the extra writes in flight only queue on the
+// link.
+
+// Publish batches: lane units v0, v0 + kExchThreads, ... (kExchUnroll of
+// them, those below `end`) loaded from `in`, then stored to a host slot.
+template <typename T>
+__device__ __forceinline__ void load_batch(const T *in, size_t v0, size_t end, bool active, T (&x)[kExchUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kExchUnroll; ++u) {
+        const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+        if (active && v < end) x[u] = in[v];
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_batch(__amdgpu_buffer_rsrc_t slot, size_t v0, size_t end,
+                                            const T (&x)[kExchUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kExchUnroll; ++u) {
+        const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
+        if (v < end) HostIO<T>::store(slot, v, x[u]);
+    }
+}
+
 // Workgroup b of an active set of `nact` owns the 8-value units
 // [nvec*b/nact, nvec*(b+1)/nact) of the call, nvec = numel / 8, and the last
 // active workgroup also owns the numel % 8 trailing values.  The split
@@ -267,11 +298,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
     __shared__ uint32_t s_status;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-
-    const uint64_t e = next_call(a, b);
-    if (e == 0 || b >= a.nactive) return;
-    const int parity = static_cast<int>(e & 1u);
-    const int rank = a.rank;
+    const bool active = b < a.nactive;
 
     const size_t nvec = a.numel / kVecElems;
     const size_t lo = nvec * static_cast<size_t>(b) / static_cast<size_t>(a.nactive);
@@ -284,6 +311,17 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
     const size_t ulo = lo * (kVecElems / per), uhi = hi * (kVecElems / per);
     const T *in = static_cast<const T *>(a.in);
     T *out = static_cast<T *>(a.out);
+
+    // the first batch of this lane's values is loaded before the call
+    // counter and the pacing wait, so its HBM latency overlaps them
+    constexpr size_t kBatch = static_cast<size_t>(kExchThreads) * kExchUnroll;
+    T x[kExchUnroll];
+    load_batch<T>(in, ulo + tid, uhi, active, x);
+
+    const uint64_t e = next_call(a, b);
+    if (e == 0 || !active) return;
+    const int parity = static_cast<int>(e & 1u);
+    const int rank = a.rank;
     __amdgpu_buffer_rsrc_t slot[W];
 #pragma unroll
     for (int q = 0; q < W; ++q)
@@ -292,18 +330,11 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
     // 1. publish this rank's slice into its host slot (write-through),
     //    paced so that each workgroup's handshake and reads start early
     pace(a, b, (hi - lo) * 16u * W);
-    for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
-        T x[kExchUnroll];
-#pragma unroll
-        for (int u = 0; u < kExchUnroll; ++u) {
-            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < uhi) x[u] = in[v];
-        }
-#pragma unroll
-        for (int u = 0; u < kExchUnroll; ++u) {
-            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < uhi) HostIO<T>::store(slot[rank], v, x[u]);
-        }
+    for (size_t v0 = ulo + tid;;) {
+        store_batch<T>(slot[rank], v0, uhi, x);
+        v0 += kBatch;
+        if (v0 >= uhi) break;
+        load_batch<T>(in, v0, uhi, true, x);
     }
     if (last && tail0 + tid < a.numel)
         HostIO<uint16_t>::store(slot[rank], tail0 + tid, static_cast<const uint16_t *>(a.in)[tail0 + tid]);
@@ -372,11 +403,7 @@ __global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
     __shared__ uint32_t s_status;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-
-    const uint64_t e = next_call(a, b);
-    if (e == 0 || b >= a.nactive) return;
-    const int parity = static_cast<int>(e & 1u);
-    const int rank = a.rank;
+    const bool active = b < a.nactive;
     const int m = a.nactive / W;               // workgroups per shard
     const int shard = b / m, j = b % m;
 
@@ -393,6 +420,16 @@ __global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
     const size_t ulo = lo * (kVecElems / per), uhi = hi * (kVecElems / per);
     const T *in = static_cast<const T *>(a.in);
     T *out = static_cast<T *>(a.out);
+
+    // first publish batch loaded ahead, as in the one-shot
+    constexpr size_t kBatch = static_cast<size_t>(kExchThreads) * kExchUnroll;
+    T x[kExchUnroll];
+    load_batch<T>(in, ulo + tid, uhi, active, x);
+
+    const uint64_t e = next_call(a, b);
+    if (e == 0 || !active) return;
+    const int parity = static_cast<int>(e & 1u);
+    const int rank = a.rank;
     __amdgpu_buffer_rsrc_t slot[W];
 #pragma unroll
     for (int q = 0; q < W; ++q)
@@ -401,18 +438,11 @@ __global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
 
     // A. publish (paced as the one-shot's)
     pace(a, b, (hi - lo) * 16u * W);
-    for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
-        T x[kExchUnroll];
-#pragma unroll
-        for (int u = 0; u < kExchUnroll; ++u) {
-            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < uhi) x[u] = in[v];
-        }
-#pragma unroll
-        for (int u = 0; u < kExchUnroll; ++u) {
-            const size_t v = v0 + static_cast<size_t>(u) * kExchThreads;
-            if (v < uhi) HostIO<T>::store(slot[rank], v, x[u]);
-        }
+    for (size_t v0 = ulo + tid;;) {
+        store_batch<T>(slot[rank], v0, uhi, x);
+        v0 += kBatch;
+        if (v0 >= uhi) break;
+        load_batch<T>(in, v0, uhi, true, x);
     }
     if (last && tail0 + tid < a.numel)
         HostIO<uint16_t>::store(slot[rank], tail0 + tid, static_cast<const uint16_t *>(a.in)[tail0 + tid]);
@@ -516,20 +546,17 @@ __global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
     const int b = blockIdx.x;
     const int tid = static_cast<int>(threadIdx.x);
     if (tid == 0) s_status = 0;
-    const uint64_t e64 = next_call(a, b);  // its barrier also orders s_status's reset
-    if (e64 == 0 || b >= a.nactive) return;
-    const uint32_t e = static_cast<uint32_t>(e64);  // the words carry the low 32 bits (never 0)
-    const int parity = static_cast<int>(e64 & 1u);
-    const int rank = a.rank;
+    const bool active = b < a.nactive;
     const size_t nunits = (a.numel + kVecElems - 1) / kVecElems;
     const size_t nvec = a.numel / kVecElems;
     const size_t lo = nunits * static_cast<size_t>(b) / static_cast<size_t>(a.nactive);
     const size_t hi = nunits * static_cast<size_t>(b + 1) / static_cast<size_t>(a.nactive);
     const size_t u = lo + static_cast<size_t>(tid);
-    const bool has = u < hi;
+    const bool has = active && u < hi;
     const uint16_t *in16 = static_cast<const uint16_t *>(a.in);
 
-    // this lane's unit of `in` (zero past numel)
+    // this lane's unit of `in` (zero past numel), loaded before the call
+    // counter so that its HBM latency overlaps the counter's
     u32x4 x = {0u, 0u, 0u, 0u};
     if (has) {
         if (VEC && u < nvec) {
@@ -543,6 +570,12 @@ __global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
             }
         }
     }
+
+    const uint64_t e64 = next_call(a, b);  // its barrier also orders s_status's reset
+    if (e64 == 0 || !active) return;
+    const uint32_t e = static_cast<uint32_t>(e64);  // the words carry the low 32 bits (never 0)
+    const int parity = static_cast<int>(e64 & 1u);
+    const int rank = a.rank;
 
     __amdgpu_buffer_rsrc_t ll[W];
 #pragma unroll
