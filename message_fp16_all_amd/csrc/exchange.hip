@@ -42,10 +42,12 @@
 // small calls.
 //
 // One-shot protocol of active workgroup b of rank r at call e:
-//   0. wait b slices (pace): the link carries requests in order, and
-//      without pacing every flag and read would queue behind all writes
-//   1. load its slice of `in` and store it to slot[e & 1][r] with
-//      system-coherent (write-through) stores                        (D2H)
+//   0. load the first batch of its slice of `in` (before the call counter,
+//      so the two latencies overlap), then wait b - 2 slices (pace): the
+//      link carries requests in order, and without pacing every flag and
+//      read would queue behind all writes
+//   1. store its slice to slot[e & 1][r] with system-coherent
+//      (write-through) stores                                        (D2H)
 //   2. every lane waits for its stores to be acknowledged; barrier; lane 0
 //      stores flag[r][b] = e at system scope -- the "fence, then flag" of
 //      the method, without a whole-cache write-back
