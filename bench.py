@@ -721,20 +721,24 @@ def profile_kernel(which, reps):
         log(f"copy: {reps} x 256 MiB")
         return
     if which == "fold":
+        # the cold protocol of the timed run: launches cycle over three
+        # workspaces (864 MiB), so none finds its inputs in the MALL
         xs = inputs.workload4()
-        _buf, ts = hr.workspace(len(xs), xs[0].size)
-        for t, x in zip(ts, xs):
-            t.copy_(to_dev(x))
-        out = torch.empty_like(ts[0])
+        wss = [hr.workspace(len(xs), xs[0].size) for _ in range(3)]
+        for _buf, ts in wss:
+            for t, x in zip(ts, xs):
+                t.copy_(to_dev(x))
+        outs = [torch.empty_like(wss[0][1][0]) for _ in range(3)]
         torch.cuda.synchronize()
-        for _ in range(reps):
-            hr.reduce(ts, out)
+        for i in range(reps):
+            hr.reduce(wss[i % 3][1], outs[i % 3])
         torch.cuda.synchronize()
+        ts = wss[0][1]
         acc = ts[0].clone()
         for t in ts[1:]:
             acc = acc + t
-        ok = bool(torch.equal(out.view(torch.int16), acc.view(torch.int16)))
-        log(f"fold G=8 N={xs[0].size}: {reps} launches, bit_exact={ok}")
+        ok = all(bool(torch.equal(o.view(torch.int16), acc.view(torch.int16))) for o in outs[:min(reps, 3)])
+        log(f"fold G=8 N={xs[0].size}: {reps} launches over 3 rotating workspaces, bit_exact={ok}")
         return
     x0b, x1b = inputs.workload2(32)
     n = x0b.size
