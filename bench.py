@@ -505,6 +505,17 @@ def fold_time_rotating_graph(c: Ctx, sets, outs, reps=30):
     return statistics.median(res)
 
 
+def fold_graph_floor(c: Ctx, calls=100):
+    """Per-call time of a graph of `calls` folds of one 16-byte unit (G = 1,
+    N = 8, one workgroup): the launch floor of a graph node on this GPU,
+    against which the decode-sized folds' graph rates are read."""
+    torch = c.torch
+    src = torch.zeros(8, dtype=torch.float16, device=c.dev)
+    dst = torch.empty_like(src)
+    t = fold_time_graph(c, [src], dst, calls)
+    return {"G": 1, "N": 8, "graph_calls": calls, "graph_us": round(t * 1e6, 3)}
+
+
 def fold_workload(c: Ctx, name, xs, prefill=False):
     torch = c.torch
     G, n = len(xs), xs[0].size
@@ -839,6 +850,8 @@ def main():
             cfgs["exchange_graph_1000_calls_N10240_one_shot"] = workload5(c, link_peak, c.hr.HR_ALGO_ONE_SHOT,
                                                                           gate_ms=args.gate_ms)
         if want("fold"):
+            log("graph node floor: one-unit fold")
+            cfgs["fold_graph_node_floor"] = fold_graph_floor(c)
             log("fold G=2 N=4096 with specials")
             cfgs["fold_G2_N4096_specials"] = fold_workload(c, "w1", c.inputs.workload1()[0])
             log("fold G=8 N=393216")
