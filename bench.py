@@ -59,7 +59,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=32)
     p.add_argument("--quick", action="store_true", help="headline only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
-    p.add_argument("--only", default="", help="comma list of sections: exchange,fold,c5,bf16")
+    p.add_argument("--only", default="", help="comma list of sections: exchange,world,fold,c5,bf16")
     p.add_argument("--profile-kernel", choices=("fold", "exchange", "copy"), default=None,
                    help="run one kernel --reps times and nothing else (for rocprofv3 counters)")
     p.add_argument("--reps", type=int, default=10)
@@ -828,6 +828,9 @@ def main():
                         r["auto"] = algo == c.hr.HR_ALGO_AUTO
                         rows.append(r)
             cfgs["exchange_2rank_host_slots"] = rows
+            log("exchange at prefill sizes (1 and 16 MiB per rank)")
+            cfgs["exchange_2rank_prefill"] = exchange_prefill(c, link_peak)
+        if want("world"):
             rows = []
             for w in (4, 8):
                 for t in (1, 8, 32):
@@ -836,13 +839,11 @@ def main():
                             continue
                         log(f"exchange world={w} tokens={t} algorithm={algo}")
                         r = exchange_workload(c, t, 300, 20, link_peak, eager_calls_n=50, world=w,
-                                              algorithm=algo)
+                                              algorithm=algo, gate_ms=args.gate_ms)
                         r.pop("_elapsed_s")
                         r.pop("_out")
                         rows.append(r)
             cfgs["exchange_world_host_slots"] = rows
-            log("exchange at prefill sizes (1 and 16 MiB per rank)")
-            cfgs["exchange_2rank_prefill"] = exchange_prefill(c, link_peak)
         if want("c5"):
             log("exchange graph of 1000 fresh calls, N=10240")
             cfgs["exchange_graph_1000_calls_N10240"] = workload5(c, link_peak, gate_ms=args.gate_ms)
