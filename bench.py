@@ -789,7 +789,7 @@ def profile_kernel(which, reps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.profile_kernel:
