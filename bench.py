@@ -319,6 +319,50 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
     }
 
 
+def group_workload(c: Ctx, tokens, steps, link_peak, world, algorithm=0, gate_ms=None):
+    """Every rank of a loopback channel in one launch per call
+    (hr_allreduce_group_f16): a graph of `steps` calls on one stream, timed
+    behind a device-side gate; checked against torch's left fold."""
+    torch, hr, inputs = c.torch, c.hr, c.inputs
+    xb = inputs.workload2(tokens) if world == 2 else inputs.workload6(world, tokens)
+    n = xb[0].size
+    x = [c.to_dev(b) for b in xb]
+    o = [torch.empty_like(t) for t in x]
+    ref = torch_fold(c, xb)
+    ch = hr.Channel(max_numel=hr.HR_DEFAULT_MAX_NUMEL, timeout_us=5_000_000, world_size=world,
+                    algorithm=algorithm)
+    taken = ch.algorithm_for(n)
+    s = torch.cuda.Stream()
+    try:
+        for _ in range(20):
+            ch.allreduce_group(x, o, s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(steps):
+                ch.allreduce_group(x, o, s)
+        if gate_ms is None:
+            gate_ms = 5.0
+        for rep in range(3):                     # two untimed (upload, settle), then the timed one
+            if rep == 2:
+                for t in o:
+                    t.zero_()
+            elapsed, _ = replay_all(c, [g], [s], gate_ms)
+        if ch.status() != hr.HR_OK:
+            raise RuntimeError(f"group exchange failed: {hr.hr_status_str(ch.status())}")
+        exact = all(same(c.np, c.to_host(t), ref) for t in o)
+        del g
+        torch.cuda.synchronize()
+    finally:
+        ch.destroy()
+    t = elapsed / steps
+    alg = (world + 1) * n * 2
+    return {"world": world, "launch": "group", "algorithm": ALGO_NAMES[taken], "tokens": tokens, "N": n,
+            "graph_us": round(t * 1e6, 3), "graph_GBps": round(alg / t / 1e9, 2),
+            "graph_frac_link": round(alg / t / 1e9 / link_peak, 4), "graph_calls": steps,
+            "bit_exact": exact}
+
+
 def exchange_prefill(c: Ctx, link_peak, sizes=(1 << 19, 1 << 23), calls=20):
     """Two-rank calls far above the decode cap (1 and 16 MiB per rank), on a
     channel made for them: paced one-shot (the automatic choice), the same
@@ -844,6 +888,14 @@ def main():
                         r.pop("_out")
                         rows.append(r)
             cfgs["exchange_world_host_slots"] = rows
+            rows = []
+            for w in (2, 4, 8):
+                for t in (1, 8, 32):
+                    for algo in (c.hr.HR_ALGO_AUTO, c.hr.HR_ALGO_ONE_SHOT, c.hr.HR_ALGO_TWO_SHOT):
+                        log(f"group launch world={w} tokens={t} algorithm={algo}")
+                        rows.append(group_workload(c, t, 300, link_peak, w, algorithm=algo,
+                                                   gate_ms=args.gate_ms))
+            cfgs["exchange_group_launch_host_slots"] = rows
         if want("c5"):
             log("exchange graph of 1000 fresh calls, N=10240")
             cfgs["exchange_graph_1000_calls_N10240"] = workload5(c, link_peak, gate_ms=args.gate_ms)

@@ -307,6 +307,37 @@ HR_API hr_status hr_allreduce_bf16(hr_channel ch, int rank, const void *in, void
                                    size_t numel, hr_stream_t stream);
 
 /*
+ * hr_allreduce_group_f16 / hr_allreduce_group_bf16 -- one all-reduce call of
+ * every rank of a loopback channel, in a single kernel launch on `stream`.
+ *
+ * Rank r's workgroups are workgroups r * num_blocks .. (r + 1) * num_blocks - 1
+ * of the launch; each runs exactly what hr_allreduce_f16 (_bf16) runs for rank
+ * r -- the same algorithm, host slots, flags and call counters -- so the
+ * result in outs[r] is the left fold of ins[0..W-1] in rank order, bit for bit
+ * what W separate calls give, and group calls and per-rank calls may follow
+ * one another on the same channel.  This is the loopback's driver for groups
+ * that have more ranks than the GPU schedules hardware queues at once: W
+ * separate launches on W loopback streams need all W queues resident
+ * together, and with eight the GPU takes turns over them; one launch of
+ * W * num_blocks <= compute-unit workgroups is resident at once.  It stands in
+ * for W GPUs each running its rank's kernel; it is not a multi-GPU call.
+ *
+ * ins, outs: world_size device buffers of numel values each (binary16, or
+ *          bfloat16 for _bf16); the arrays are copied into the launch and may
+ *          be freed on return.  outs[r] == ins[r] is allowed; any other
+ *          overlap between rank r's output and any rank's input or output is
+ *          an error.
+ * numel, errors, sticky status, capture: as hr_allreduce_f16.  The launch
+ *          needs every compute unit able to take one of its workgroups; work
+ *          that fills the device meanwhile delays it (the watchdog bounds the
+ *          wait).
+ */
+HR_API hr_status hr_allreduce_group_f16(hr_channel ch, const void *const *ins, void *const *outs, size_t numel,
+                                        hr_stream_t stream);
+HR_API hr_status hr_allreduce_group_bf16(hr_channel ch, const void *const *ins, void *const *outs, size_t numel,
+                                         hr_stream_t stream);
+
+/*
  * hr_channel_status -- the channel's sticky asynchronous status: HR_OK, or
  * HR_ERR_TIMEOUT / HR_ERR_ABORTED once a kernel has recorded one.  Reads a
  * host-mapped word; it does not synchronise, so synchronise the rank streams

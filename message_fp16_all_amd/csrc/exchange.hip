@@ -296,9 +296,8 @@ __device__ __forceinline__ void store_batch(__amdgpu_buffer_rsrc_t slot, size_t 
 // (all buffers 16-byte aligned) or one value (2-byte aligned buffers); E is
 // the element type (binary16 or bfloat16).
 template <int W, bool VEC, class E>
-__global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
+__device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
     __shared__ uint32_t s_status;
-    const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const bool active = b < a.nactive;
 
@@ -401,9 +400,8 @@ __global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
 // so every peer had finished call e, including its reads of slot and
 // reduced-slot parity e & 1, before the rank starts call e + 2.
 template <int W, bool VEC, class E>
-__global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
+__device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
     __shared__ uint32_t s_status;
-    const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const bool active = b < a.nactive;
     const int m = a.nactive / W;               // workgroups per shard
@@ -550,9 +548,8 @@ constexpr bool kLLAckFirst = false;        // first poll after the own words are
 constexpr int kLLSleep = 1;                // s_sleep after a failed poll (x 64 clocks)
 
 template <int W, bool VEC, class E>
-__global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
+__device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b) {
     __shared__ uint32_t s_status;
-    const int b = blockIdx.x;
     const int tid = static_cast<int>(threadIdx.x);
     if (tid == 0) s_status = 0;
     const bool active = b < a.nactive;
@@ -664,6 +661,57 @@ __global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
             if (i < a.numel) out16[i] = static_cast<uint16_t>(acc[k / 2] >> (16 * (k % 2)));
         }
     }
+}
+
+// One launch per rank: workgroup b of the rank named in the arguments.
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange_k(ExchArgs a) {
+    exchange_body<W, VEC, E>(a, static_cast<int>(blockIdx.x));
+}
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange2_k(ExchArgs a) {
+    exchange2_body<W, VEC, E>(a, static_cast<int>(blockIdx.x));
+}
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange_ll_k(ExchArgs a) {
+    exchange_ll_body<W, VEC, E>(a, static_cast<int>(blockIdx.x));
+}
+
+// One launch for every rank of a loopback group: workgroups
+// [r * nblocks, (r + 1) * nblocks) are rank r's workgroups 0 .. nblocks - 1,
+// with rank r's buffers and call counters.  They run the same protocol
+// through the same host slots and flags as W separate launches would; the
+// grid (W * nblocks <= compute units) is resident at once, so no rank waits
+// for a hardware queue to be scheduled.
+struct GroupArgs {
+    ExchArgs a;  // rank and buffers are per workgroup below
+    const void *in[kMaxWorld];
+    void *out[kMaxWorld];
+};
+
+__device__ __forceinline__ ExchArgs group_rank_args(const GroupArgs &g, int rank) {
+    ExchArgs a = g.a;
+    a.rank = rank;
+    a.in = g.in[rank];
+    a.out = g.out[rank];
+    a.epochs = g.a.epochs + static_cast<size_t>(rank) * static_cast<size_t>(g.a.nblocks);
+    return a;
+}
+
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange_group_k(GroupArgs g) {
+    const int rank = static_cast<int>(blockIdx.x) / g.a.nblocks;
+    exchange_body<W, VEC, E>(group_rank_args(g, rank), static_cast<int>(blockIdx.x) - rank * g.a.nblocks);
+}
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange2_group_k(GroupArgs g) {
+    const int rank = static_cast<int>(blockIdx.x) / g.a.nblocks;
+    exchange2_body<W, VEC, E>(group_rank_args(g, rank), static_cast<int>(blockIdx.x) - rank * g.a.nblocks);
+}
+template <int W, bool VEC, class E>
+__global__ __launch_bounds__(kExchThreads) void exchange_ll_group_k(GroupArgs g) {
+    const int rank = static_cast<int>(blockIdx.x) / g.a.nblocks;
+    exchange_ll_body<W, VEC, E>(group_rank_args(g, rank), static_cast<int>(blockIdx.x) - rank * g.a.nblocks);
 }
 
 // Link calibration: workgroups [0, nw) store `units` 16-byte units of `src`
@@ -780,6 +828,43 @@ void launch_exchange(const ExchArgs &a, bool vec, Algo algo, hipStream_t s) {
         hipLaunchKernelGGL((exchange_k<W, true, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
     else
         hipLaunchKernelGGL((exchange_k<W, false, E>), dim3(a.nblocks), dim3(kExchThreads), 0, s, a);
+}
+
+template <int W, class E>
+void launch_group(const GroupArgs &g, bool vec, Algo algo, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(W * g.a.nblocks));
+    if (algo == Algo::ll) {
+        if (vec)
+            hipLaunchKernelGGL((exchange_ll_group_k<W, true, E>), grid, dim3(kExchThreads), 0, s, g);
+        else
+            hipLaunchKernelGGL((exchange_ll_group_k<W, false, E>), grid, dim3(kExchThreads), 0, s, g);
+        return;
+    }
+    if (algo == Algo::two_shot) {
+        if (vec)
+            hipLaunchKernelGGL((exchange2_group_k<W, true, E>), grid, dim3(kExchThreads), 0, s, g);
+        else
+            hipLaunchKernelGGL((exchange2_group_k<W, false, E>), grid, dim3(kExchThreads), 0, s, g);
+        return;
+    }
+    if (vec)
+        hipLaunchKernelGGL((exchange_group_k<W, true, E>), grid, dim3(kExchThreads), 0, s, g);
+    else
+        hipLaunchKernelGGL((exchange_group_k<W, false, E>), grid, dim3(kExchThreads), 0, s, g);
+}
+
+template <class E>
+void launch_group_w(const GroupArgs &g, bool vec, Algo algo, hipStream_t s) {
+    switch (g.a.world) {
+        case 2: launch_group<2, E>(g, vec, algo, s); break;
+        case 3: launch_group<3, E>(g, vec, algo, s); break;
+        case 4: launch_group<4, E>(g, vec, algo, s); break;
+        case 5: launch_group<5, E>(g, vec, algo, s); break;
+        case 6: launch_group<6, E>(g, vec, algo, s); break;
+        case 7: launch_group<7, E>(g, vec, algo, s); break;
+        case 8: launch_group<8, E>(g, vec, algo, s); break;
+        default: break;
+    }
 }
 
 template <class E>
@@ -988,25 +1073,10 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
 
 namespace {
 
-template <class E>
-hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, size_t numel, hr_stream_t stream) {
-    if (ch == nullptr || rank < 0 || rank >= ch->world_size) return HR_ERR_INVALID_ARG;
-    const uint32_t sticky = __atomic_load_n(
-        reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->error_off), __ATOMIC_ACQUIRE);
-    if (sticky != 0) return static_cast<hr_status>(sticky);
-    if (numel == 0) return HR_OK;
-    if (in == nullptr || out == nullptr) return HR_ERR_INVALID_ARG;
-    if (numel > ch->max_numel) return HR_ERR_TOO_LARGE;
-    if (!aligned(in, 2) || !aligned(out, 2)) return HR_ERR_ALIGNMENT;
-    if (partial_overlap(in, out, numel * 2)) return HR_ERR_INVALID_ARG;
-
-    int dev = -1;
-    if (stream_device(stream, &dev) != hipSuccess) return HR_ERR_HIP;
-    if (dev != ch->device) return HR_ERR_INVALID_ARG;
-
+// The launch arguments of a call of numel values by `rank` (buffers left
+// unset), and the algorithm the call takes.
+ExchArgs call_args(hr_channel ch, int rank, size_t numel, Algo *algo_out) {
     ExchArgs a{};
-    a.in = in;
-    a.out = out;
     a.numel = numel;
     a.slots = reinterpret_cast<uint16_t *>(ch->host_dev);
     a.stride = ch->stride;
@@ -1030,7 +1100,82 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
                 : algo == Algo::ll     ? active_blocks_ll(numel)
                                        : active_blocks(numel, ch->nblocks, ch->world_size);
 
+    *algo_out = algo;
+    return a;
+}
+
+template <class E>
+hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, size_t numel, hr_stream_t stream) {
+    if (ch == nullptr || rank < 0 || rank >= ch->world_size) return HR_ERR_INVALID_ARG;
+    const uint32_t sticky = __atomic_load_n(
+        reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->error_off), __ATOMIC_ACQUIRE);
+    if (sticky != 0) return static_cast<hr_status>(sticky);
+    if (numel == 0) return HR_OK;
+    if (in == nullptr || out == nullptr) return HR_ERR_INVALID_ARG;
+    if (numel > ch->max_numel) return HR_ERR_TOO_LARGE;
+    if (!aligned(in, 2) || !aligned(out, 2)) return HR_ERR_ALIGNMENT;
+    if (partial_overlap(in, out, numel * 2)) return HR_ERR_INVALID_ARG;
+
+    int dev = -1;
+    if (stream_device(stream, &dev) != hipSuccess) return HR_ERR_HIP;
+    if (dev != ch->device) return HR_ERR_INVALID_ARG;
+
+    Algo algo;
+    ExchArgs a = call_args(ch, rank, numel, &algo);
+    a.in = in;
+    a.out = out;
     launch_exchange_w<E>(a, aligned(in, 16) && aligned(out, 16), algo, reinterpret_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
+}
+
+// True when [a, a+bytes) and [b, b+bytes) share a byte (equal pointers too).
+inline bool ranges_overlap(const void *a, const void *b, size_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bytes && y < x + bytes;
+}
+
+// Every rank of the channel in one launch (the loopback group).
+template <class E>
+hr_status group_impl(hr_channel ch, const void *const *ins, void *const *outs, size_t numel, hr_stream_t stream) {
+    if (ch == nullptr) return HR_ERR_INVALID_ARG;
+    const uint32_t sticky = __atomic_load_n(
+        reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->error_off), __ATOMIC_ACQUIRE);
+    if (sticky != 0) return static_cast<hr_status>(sticky);
+    if (numel == 0) return HR_OK;
+    if (ins == nullptr || outs == nullptr) return HR_ERR_INVALID_ARG;
+    if (numel > ch->max_numel) return HR_ERR_TOO_LARGE;
+    const int W = ch->world_size;
+    const size_t bytes = numel * 2;
+    bool vec = true;
+    for (int r = 0; r < W; ++r) {
+        if (ins[r] == nullptr || outs[r] == nullptr) return HR_ERR_INVALID_ARG;
+        if (!aligned(ins[r], 2) || !aligned(outs[r], 2)) return HR_ERR_ALIGNMENT;
+        vec = vec && aligned(ins[r], 16) && aligned(outs[r], 16);
+    }
+    // A rank may fold in place (out == in); any other overlap would let one
+    // rank's output change what another rank publishes or re-reads.
+    for (int r = 0; r < W; ++r) {
+        if (partial_overlap(ins[r], outs[r], bytes)) return HR_ERR_INVALID_ARG;
+        for (int q = 0; q < W; ++q) {
+            if (q == r) continue;
+            if (ranges_overlap(outs[r], outs[q], bytes) || ranges_overlap(outs[r], ins[q], bytes))
+                return HR_ERR_INVALID_ARG;
+        }
+    }
+
+    int dev = -1;
+    if (stream_device(stream, &dev) != hipSuccess) return HR_ERR_HIP;
+    if (dev != ch->device) return HR_ERR_INVALID_ARG;
+
+    Algo algo;
+    GroupArgs g{};
+    g.a = call_args(ch, 0, numel, &algo);
+    g.a.epochs = ch->dev_epochs;  // rank r's counters follow at r * nblocks
+    for (int r = 0; r < W; ++r) {
+        g.in[r] = ins[r];
+        g.out[r] = outs[r];
+    }
+    launch_group_w<E>(g, vec, algo, reinterpret_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
 }
 
@@ -1044,6 +1189,16 @@ extern "C" HR_API hr_status hr_allreduce_f16(hr_channel ch, int rank, const void
 extern "C" HR_API hr_status hr_allreduce_bf16(hr_channel ch, int rank, const void *in, void *out, size_t numel,
                                               hr_stream_t stream) {
     return allreduce_impl<BF16>(ch, rank, in, out, numel, stream);
+}
+
+extern "C" HR_API hr_status hr_allreduce_group_f16(hr_channel ch, const void *const *ins, void *const *outs,
+                                                   size_t numel, hr_stream_t stream) {
+    return group_impl<F16>(ch, ins, outs, numel, stream);
+}
+
+extern "C" HR_API hr_status hr_allreduce_group_bf16(hr_channel ch, const void *const *ins, void *const *outs,
+                                                    size_t numel, hr_stream_t stream) {
+    return group_impl<BF16>(ch, ins, outs, numel, stream);
 }
 
 extern "C" HR_API hr_status hr_exchange_algorithm(hr_channel ch, size_t numel, int *algorithm) {

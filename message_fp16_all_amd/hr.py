@@ -45,7 +45,8 @@ EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel
            "hr_channel_abort", "hr_channel_get_info", "hr_destroy", "hr_status_str",
            "hr_loopback_stream_create", "hr_loopback_stream_destroy",
            "hr_reduce_bf16", "hr_allreduce_bf16", "hr_admit", "hr_route_str", "hr_decode_numel",
-           "hr_workspace_stride", "hr_exchange_algorithm")
+           "hr_workspace_stride", "hr_exchange_algorithm", "hr_allreduce_group_f16",
+           "hr_allreduce_group_bf16")
 
 HR_ROUTE_HOST = 0
 HR_DECLINE_DISABLED = 1
@@ -126,6 +127,8 @@ def load() -> ctypes.CDLL:
     lib.hr_allreduce_f16.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
     lib.hr_reduce_f16.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.hr_allreduce_bf16.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+    lib.hr_allreduce_group_f16.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_size_t, vp]
+    lib.hr_allreduce_group_bf16.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_size_t, vp]
     lib.hr_reduce_bf16.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.hr_channel_status.argtypes = [vp]
     lib.hr_exchange_algorithm.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
@@ -185,6 +188,21 @@ def hr_allreduce_bf16(ch: int, rank: int, in_ptr: int, out_ptr: int, numel: int,
                       stream: int) -> int:
     """Raw call; returns the hr_status code."""
     return load().hr_allreduce_bf16(ch, rank, in_ptr, out_ptr, numel, stream)
+
+
+def hr_allreduce_group_f16(ch: int, in_ptrs, out_ptrs, numel: int, stream: int) -> int:
+    """Raw call; ``in_ptrs``/``out_ptrs`` are sequences of world_size device
+    addresses (None for a null pointer).  Returns the hr_status code."""
+    ins = (ctypes.c_void_p * max(1, len(in_ptrs)))(*in_ptrs)
+    outs = (ctypes.c_void_p * max(1, len(out_ptrs)))(*out_ptrs)
+    return load().hr_allreduce_group_f16(ch, ins, outs, numel, stream)
+
+
+def hr_allreduce_group_bf16(ch: int, in_ptrs, out_ptrs, numel: int, stream: int) -> int:
+    """As hr_allreduce_group_f16 for bfloat16 buffers."""
+    ins = (ctypes.c_void_p * max(1, len(in_ptrs)))(*in_ptrs)
+    outs = (ctypes.c_void_p * max(1, len(out_ptrs)))(*out_ptrs)
+    return load().hr_allreduce_group_bf16(ch, ins, outs, numel, stream)
 
 
 def hr_reduce_bf16(ptrs, G: int, out_ptr: int, numel: int, stream: int) -> int:
@@ -337,6 +355,25 @@ class Channel:
         _check(fn(self.handle, rank, _f16_ptr(inp, "in", dt), _f16_ptr(out, "out", dt), n,
                   _stream_handle(stream, out)), name)
         return out
+
+    def allreduce_group(self, ins, outs, stream=None):
+        """Every rank's call in one launch (loopback): ``ins[r]``/``outs[r]``
+        are rank r's torch.float16 or torch.bfloat16 tensors."""
+        import torch
+        if len(ins) != self.world_size or len(outs) != self.world_size:
+            raise ValueError(f"expected {self.world_size} inputs and outputs")
+        n = ins[0].numel()
+        bf = ins[0].dtype == torch.bfloat16
+        dt = torch.bfloat16 if bf else torch.float16
+        for r in range(self.world_size):
+            if ins[r].numel() != n or outs[r].numel() != n:
+                raise ValueError(f"rank {r}: every input and output must hold {n} values")
+        ip = [_f16_ptr(t, f"ins[{r}]", dt) for r, t in enumerate(ins)]
+        op = [_f16_ptr(t, f"outs[{r}]", dt) for r, t in enumerate(outs)]
+        fn, name = ((hr_allreduce_group_bf16, "hr_allreduce_group_bf16") if bf
+                    else (hr_allreduce_group_f16, "hr_allreduce_group_f16"))
+        _check(fn(self.handle, ip, op, n, _stream_handle(stream, outs[0])), name)
+        return outs
 
     def status(self) -> int:
         return hr_channel_status(self.handle)

@@ -101,6 +101,8 @@ def test_channel_validation_before_any_device_call():
         cfg = hr.hr_channel_config(0, 2, 0, 0, 0, 0, rate)
         assert lib.hr_create_channel(ctypes.byref(cfg), ctypes.byref(h)) == hr.HR_ERR_INVALID_ARG
     assert hr.hr_allreduce_f16(None, 0, FAKE, FAKE, 16, 0) == hr.HR_ERR_INVALID_ARG
+    assert hr.hr_allreduce_group_f16(None, [FAKE, FAKE], [FAKE, FAKE], 16, 0) == hr.HR_ERR_INVALID_ARG
+    assert hr.hr_allreduce_group_bf16(None, [FAKE, FAKE], [FAKE, FAKE], 16, 0) == hr.HR_ERR_INVALID_ARG
     assert hr.hr_exchange_algorithm.__doc__
     assert lib.hr_exchange_algorithm(None, 16, None) == hr.HR_ERR_INVALID_ARG
     assert hr.hr_channel_status(None) == hr.HR_ERR_INVALID_ARG
