@@ -106,7 +106,9 @@ typedef enum {
 /* Exchange algorithm of a channel (all produce the same bits). */
 #define HR_ALGO_AUTO 0      /* two ranks: low-latency up to 12288 values,
                                one-shot above; 3+ ranks: one-shot, and
-                               two-shot from 32768 values                 */
+                               two-shot from a size that falls with the
+                               group (98304 values at 3 ranks, 16384 at 4
+                               and 5, 8192 at 6, 4096 at 7 and 8)       */
 #define HR_ALGO_ONE_SHOT 1  /* every rank reads every peer's contribution */
 #define HR_ALGO_TWO_SHOT 2  /* shard owners fold, then everyone gathers;
                                needs num_blocks >= world_size             */

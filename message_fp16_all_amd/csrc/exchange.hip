@@ -782,8 +782,21 @@ inline int active_blocks(size_t numel, int nblocks, int world) {
 }
 
 // Groups of three or more take the two-shot from this many values under the
-// automatic choice; the second handshake doubles the latency of small calls.
-constexpr size_t kTwoShotMinNumel = 32768;
+// automatic choice: the one-shot reads W - 1 peers' whole contributions, the
+// two-shot 2 (W - 1) / W of one, but its second handshake adds latency, so
+// the crossover falls as the group grows.  Measured on MI355X with every rank
+// in one group launch (graph-captured), as the first of 512 .. 131072 values
+// at which the two-shot was faster: W = 3 98304, W = 4 and 5 16384, W = 6
+// 8192, W = 7 and 8 4096.
+inline size_t two_shot_min_numel(int world) {
+    switch (world) {
+        case 3: return 98304;
+        case 4:
+        case 5: return 16384;
+        case 6: return 8192;
+        default: return 4096;
+    }
+}
 
 enum class Algo { one_shot, two_shot, ll };
 
@@ -793,8 +806,8 @@ enum class Algo { one_shot, two_shot, ll };
 // asks for an algorithm it cannot take gets the one-shot (same bits).
 // Automatic choice: for two ranks LL up to kLLAutoMaxNumel values and the
 // one-shot above; for three or more the one-shot, and the two-shot from
-// kTwoShotMinNumel (LL's readers poll every peer's data, which costs more
-// than it saves there).
+// two_shot_min_numel(W) (LL's readers poll every peer's data, which costs
+// more than it saves there).
 inline Algo choose_algo(int algorithm, size_t numel, int world, int nblocks) {
     const bool ll_ok = numel <= kLLMaxNumel && active_blocks_ll(numel) <= nblocks;
     const bool two_ok = nblocks >= world;
@@ -805,7 +818,7 @@ inline Algo choose_algo(int algorithm, size_t numel, int world, int nblocks) {
         default: break;
     }
     if (world == 2 && ll_ok && numel <= kLLAutoMaxNumel) return Algo::ll;
-    return (two_ok && world >= 3 && numel >= kTwoShotMinNumel) ? Algo::two_shot : Algo::one_shot;
+    return (two_ok && world >= 3 && numel >= two_shot_min_numel(world)) ? Algo::two_shot : Algo::one_shot;
 }
 
 template <int W, class E>

@@ -428,8 +428,15 @@ def test_algorithm_choice():
         assert ch2l.algorithm_for(32_768) == hr.HR_ALGO_LL
         assert ch2l.algorithm_for(32_769) == hr.HR_ALGO_ONE_SHOT
         assert ch4.algorithm_for(10_240) == hr.HR_ALGO_ONE_SHOT
-        assert ch4.algorithm_for(32_767) == hr.HR_ALGO_ONE_SHOT
-        assert ch4.algorithm_for(32_768) == hr.HR_ALGO_TWO_SHOT
+        assert ch4.algorithm_for(16_383) == hr.HR_ALGO_ONE_SHOT
+        assert ch4.algorithm_for(16_384) == hr.HR_ALGO_TWO_SHOT
+        for W, first in ((3, 98_304), (5, 16_384), (6, 8192), (7, 4096), (8, 4096)):
+            chw = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
+            try:
+                assert chw.algorithm_for(first - 1) == hr.HR_ALGO_ONE_SHOT, W
+                assert chw.algorithm_for(first) == hr.HR_ALGO_TWO_SHOT, W
+            finally:
+                chw.destroy()
         assert ch4o.algorithm_for(4096) == hr.HR_ALGO_ONE_SHOT
         with pytest.raises(hr.HrError) as ei:
             ch2.algorithm_for(hr.HR_DEFAULT_MAX_NUMEL + 1)

@@ -171,14 +171,14 @@ def test_missing_rank_times_out_every_waiting_rank(algo):
 
 
 def test_automatic_choice_mixes_algorithms_across_calls():
-    """Under HR_ALGO_AUTO a W = 4 channel takes the one-shot below 32768
+    """Under HR_ALGO_AUTO a W = 4 channel takes the one-shot below 16384
     values and the two-shot from there; alternating sizes alternate the
     algorithm while the slot parity keeps advancing."""
     W = 4
     streams = hr.LoopbackStreams(0, n=W)
     ch = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
     try:
-        for call, n in enumerate([4096, 131_072, 32_767, 32_768, 9, 65_539, 10_241, 10_240]):
+        for call, n in enumerate([4096, 131_072, 16_383, 16_384, 9, 65_539, 10_241, 32_768]):
             xb = [specials_mix(n, seed=500 + 10 * call + r) for r in range(W)]
             xs = [to_dev(b) for b in xb]
             outs = [torch.empty_like(x) for x in xs]
