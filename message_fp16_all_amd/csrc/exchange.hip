@@ -536,7 +536,21 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
 // stores nothing.  A word of an earlier use of the parity holds e - 2, never
 // e; parity safety is the one-shot's argument, with "flag" read as "word".
 constexpr size_t kLLMaxNumel = 32768;      // values per call the LL slots hold
-constexpr size_t kLLAutoMaxNumel = 12288;  // automatic choice takes LL up to here (24 KiB)
+// Largest call the automatic choice gives LL: its doubled bytes and its
+// readers polling every peer's data cost more as the group grows.  Measured
+// on MI355X, graph-captured (two ranks on two loopback streams, larger groups
+// in one group launch), as the largest size at which LL beat the one-shot:
+// W = 2 12288, W = 3 6144, W = 4 3072, W = 5 and 6 1024, W = 7 and 8 512.
+inline size_t ll_auto_max_numel(int world) {
+    switch (world) {
+        case 2: return 12288;
+        case 3: return 6144;
+        case 4: return 3072;
+        case 5:
+        case 6: return 1024;
+        default: return 512;
+    }
+}
 // A lane polls as soon as its own words are issued and sleeps only briefly
 // between polls.  Measured on MI355X, two ranks in loopback, graph-captured,
 // against waiting for the own stores' acknowledgement before the first poll
@@ -804,10 +818,9 @@ enum class Algo { one_shot, two_shot, ll };
 // of a rank's buffers), so every rank of a call takes the same one.  LL needs
 // a call of at most kLLMaxNumel values (and one lane per unit); a call that
 // asks for an algorithm it cannot take gets the one-shot (same bits).
-// Automatic choice: for two ranks LL up to kLLAutoMaxNumel values and the
-// one-shot above; for three or more the one-shot, and the two-shot from
-// two_shot_min_numel(W) (LL's readers poll every peer's data, which costs
-// more than it saves there).
+// Automatic choice: LL up to ll_auto_max_numel(W) values; above that, for
+// two ranks the one-shot, for three or more the one-shot and, from
+// two_shot_min_numel(W), the two-shot.
 inline Algo choose_algo(int algorithm, size_t numel, int world, int nblocks) {
     const bool ll_ok = numel <= kLLMaxNumel && active_blocks_ll(numel) <= nblocks;
     const bool two_ok = nblocks >= world;
@@ -817,7 +830,7 @@ inline Algo choose_algo(int algorithm, size_t numel, int world, int nblocks) {
         case HR_ALGO_LL: return ll_ok ? Algo::ll : Algo::one_shot;
         default: break;
     }
-    if (world == 2 && ll_ok && numel <= kLLAutoMaxNumel) return Algo::ll;
+    if (ll_ok && numel <= ll_auto_max_numel(world)) return Algo::ll;
     return (two_ok && world >= 3 && numel >= two_shot_min_numel(world)) ? Algo::two_shot : Algo::one_shot;
 }
 

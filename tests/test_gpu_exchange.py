@@ -430,9 +430,15 @@ def test_algorithm_choice():
         assert ch4.algorithm_for(10_240) == hr.HR_ALGO_ONE_SHOT
         assert ch4.algorithm_for(16_383) == hr.HR_ALGO_ONE_SHOT
         assert ch4.algorithm_for(16_384) == hr.HR_ALGO_TWO_SHOT
-        for W, first in ((3, 98_304), (5, 16_384), (6, 8192), (7, 4096), (8, 4096)):
+        assert ch4.algorithm_for(3072) == hr.HR_ALGO_LL
+        assert ch4.algorithm_for(3073) == hr.HR_ALGO_ONE_SHOT
+        for W, ll_max, first in ((3, 6144, 98_304), (5, 1024, 16_384), (6, 1024, 8192), (7, 512, 4096),
+                                 (8, 512, 4096)):
             chw = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
             try:
+                assert chw.algorithm_for(1) == hr.HR_ALGO_LL, W
+                assert chw.algorithm_for(ll_max) == hr.HR_ALGO_LL, W
+                assert chw.algorithm_for(ll_max + 1) == hr.HR_ALGO_ONE_SHOT, W
                 assert chw.algorithm_for(first - 1) == hr.HR_ALGO_ONE_SHOT, W
                 assert chw.algorithm_for(first) == hr.HR_ALGO_TWO_SHOT, W
             finally:

@@ -171,9 +171,9 @@ def test_missing_rank_times_out_every_waiting_rank(algo):
 
 
 def test_automatic_choice_mixes_algorithms_across_calls():
-    """Under HR_ALGO_AUTO a W = 4 channel takes the one-shot below 16384
-    values and the two-shot from there; alternating sizes alternate the
-    algorithm while the slot parity keeps advancing."""
+    """Under HR_ALGO_AUTO a W = 4 channel takes LL up to 3072 values, the
+    one-shot below 16384 and the two-shot from there; alternating sizes
+    alternate the algorithm while the slot parity keeps advancing."""
     W = 4
     streams = hr.LoopbackStreams(0, n=W)
     ch = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
