@@ -19,7 +19,10 @@
 // Three algorithms, one channel, the same bits (a call takes one of them as
 // a function of the channel and numel, so every rank agrees): the one-shot
 // below (the source's method), the two-shot (exchange2_k) and the
-// low-latency one-shot for small calls (exchange_ll_k).
+// low-latency one-shot for small calls (exchange_ll_k).  Each is a device
+// body of the workgroup index, launched either once per rank (the rank's
+// own kernel, as on its own GPU) or once for every rank of a loopback group
+// (the *_group_k kernels: rank r's workgroups are blocks r * nblocks ..).
 //
 // Channel memory
 //   host (pinned, device-mapped, fine-grained/coherent):
