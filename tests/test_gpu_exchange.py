@@ -560,3 +560,31 @@ def test_prefill_sized_calls(streams, algorithm):
     finally:
         torch.cuda.synchronize()
         ch.destroy()
+
+
+@pytest.mark.parametrize("algorithm", [hr.HR_ALGO_AUTO, hr.HR_ALGO_TWO_SHOT], ids=["auto", "two-shot"])
+def test_channel_at_the_size_limit(streams, algorithm):
+    """One call of HR_MAX_NUMEL_LIMIT values (1 GiB per rank) on a channel of
+    that size, where slot offsets reach 2^30 bytes: every rank's output is
+    checked against the oracle on a million seeded sample positions and on
+    the first and last 4096 values."""
+    n = hr.HR_MAX_NUMEL_LIMIT
+    rng = np.random.default_rng(2029)
+    x0b = rng.integers(0, 1 << 16, n, dtype=np.uint16)   # every pattern class, NaN and inf included
+    x1b = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    say(f"exchange: channel at the size limit, n={n}, algorithm {algorithm}")
+    ch = hr.Channel(max_numel=n, timeout_us=TIMEOUT_US, algorithm=algorithm)
+    try:
+        x0, x1 = to_dev(x0b), to_dev(x1b)
+        out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+        loopback(ch, x0, x1, out0, out1, streams)
+        idx = np.unique(np.concatenate([rng.integers(0, n, 1_000_000), np.arange(4096),
+                                        np.arange(n - 4096, n)]))
+        ref = oracle.add(x0b[idx], x1b[idx])
+        for r, out in enumerate((out0, out1)):
+            got = to_host(out)[idx]
+            assert_same_bits(got, ref, f"size-limit call rank {r}")
+        del x0, x1, out0, out1
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
