@@ -7,7 +7,9 @@
  *   1. folds them with hr_reduce_f16 into out0,
  *   2. if G == 2, runs one two-rank loopback hr_allreduce_f16 on two streams
  *      from hr_loopback_stream_create, into out1 (rank 0) and out2 (rank 1),
- * and writes out0 [out1 out2] to <out.bin>.  The test that builds and runs
+ *   3. if 2 <= G <= HR_MAX_WORLD, runs one hr_allreduce_group_f16 of all G
+ *      ranks on a G-rank channel (one launch), into G more outputs,
+ * and writes out0 [out1 out2] [G group outputs] to <out.bin>.  The test that builds and runs
  * it compares the outputs with the oracle.  Exit status: 0 on success.
  *
  * usage: hr_c_client G N in.bin out.bin
@@ -50,19 +52,19 @@ int main(int argc, char **argv)
         return 1;
 
     uint16_t *host = (uint16_t *)malloc((size_t)G * n * 2);
-    uint16_t *res = (uint16_t *)malloc(3 * n * 2);
+    uint16_t *res = (uint16_t *)malloc((size_t)(3 + G) * n * 2);
     FILE *f = fopen(argv[3], "rb");
     if (!host || !res || !f || fread(host, 2, (size_t)G * n, f) != (size_t)G * n)
         return 1;
     fclose(f);
 
     void *dev[HR_MAX_G];
-    void *out[3];
+    void *out[3 + HR_MAX_G];
     for (int g = 0; g < G; ++g) {
         CHECK_HIP(hipMalloc(&dev[g], n * 2));
         CHECK_HIP(hipMemcpy(dev[g], host + (size_t)g * n, n * 2, hipMemcpyHostToDevice));
     }
-    for (int k = 0; k < 3; ++k)
+    for (int k = 0; k < 3 + G; ++k)
         CHECK_HIP(hipMalloc(&out[k], n * 2));
 
     hr_stream_t s0 = NULL, s1 = NULL;
@@ -89,6 +91,19 @@ int main(int argc, char **argv)
         CHECK_HR(hr_loopback_stream_destroy(s1));
         written = 3 * n;
     }
+    if (G >= 2 && G <= HR_MAX_WORLD) {
+        hr_channel ch = NULL;
+        hr_channel_config cfg = {.device = 0, .world_size = G, .max_numel = n, .timeout_us = 2000000u,
+                                 .algorithm = HR_ALGO_AUTO};
+        CHECK_HR(hr_create_channel(&cfg, &ch));
+        CHECK_HR(hr_allreduce_group_f16(ch, (const void *const *)dev, (void *const *)(out + 3), n, s0));
+        CHECK_HIP(hipStreamSynchronize((hipStream_t)s0));
+        CHECK_HR(hr_channel_status(ch));
+        for (int r = 0; r < G; ++r)
+            CHECK_HIP(hipMemcpy(res + written + (size_t)r * n, out[3 + r], n * 2, hipMemcpyDeviceToHost));
+        written += (size_t)G * n;
+        CHECK_HR(hr_destroy(ch));
+    }
     CHECK_HR(hr_loopback_stream_destroy(s0));
 
     f = fopen(argv[4], "wb");
@@ -97,7 +112,7 @@ int main(int argc, char **argv)
     fclose(f);
     for (int g = 0; g < G; ++g)
         CHECK_HIP(hipFree(dev[g]));
-    for (int k = 0; k < 3; ++k)
+    for (int k = 0; k < 3 + G; ++k)
         CHECK_HIP(hipFree(out[k]));
     free(host);
     free(res);

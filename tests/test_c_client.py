@@ -58,6 +58,8 @@ def test_c_client_matches_oracle(tmp_path, G, n):
     got = np.frombuffer((tmp_path / "out.bin").read_bytes(), dtype=np.uint16)
     ref = oracle.fold(xs)
     parts = got.reshape(-1, n)
-    assert parts.shape[0] == (3 if G == 2 else 1)
+    # the fold; for two ranks the per-rank exchange's two outputs; for groups
+    # of up to eight the group launch's G outputs
+    assert parts.shape[0] == 1 + (2 if G == 2 else 0) + (G if 2 <= G <= hr.HR_MAX_WORLD else 0)
     for p in parts:
         assert oracle.same_bits(p, ref).all()
