@@ -248,6 +248,17 @@ HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out
  * one process, streams from hr_loopback_stream_create), each endpoint by one
  * stream at a time; all launches of a call must be in flight together or the
  * waits time out.
+ * Null-stream hazard in loopback: the Algorithmiq page "fix(group): run each
+ * rank on a non-blocking stream" ("What") runs every rank on a non-blocking
+ * stream.  The streams of hr_loopback_stream_create are not non-blocking
+ * (HIP gives a compute-unit-mask stream no flags): they wait for earlier
+ * null-stream work, and later null-stream work waits for them.  Work put on
+ * the null stream between the ranks' launches of one call therefore holds
+ * back the ranks launched after it while the ones launched before it spin:
+ * the call ends at the watchdog with the sticky HR_ERR_TIMEOUT.  Enqueue no
+ * null-stream work (including a library's default-stream work) between the
+ * launches of one call, or use hr_allreduce_group_f16, whose one launch has
+ * no such window.
  *
  * Errors: HR_ERR_INVALID_ARG, HR_ERR_ALIGNMENT, HR_ERR_TOO_LARGE (the caller
  * keeps its own collective for larger payloads), HR_ERR_HIP; and the
@@ -343,19 +354,41 @@ HR_API hr_status hr_allreduce_group_bf16(hr_channel ch, const void *const *ins, 
 
 /*
  * hr_channel_status -- the channel's sticky asynchronous status: HR_OK, or
- * HR_ERR_TIMEOUT / HR_ERR_ABORTED once a kernel has recorded one.  Reads a
- * host-mapped word; it does not synchronise, so synchronise the rank streams
- * first to see the outcome of work already enqueued.  Recovery from an error
- * is hr_destroy followed by hr_create_channel.
+ * HR_ERR_TIMEOUT / HR_ERR_ABORTED once a kernel has recorded one.
+ *
+ * A collective that spins on its peer has no timeout of its own; the
+ * openinfer pull request "fix(qwen3): re-enable CUDA Graph under TP via
+ * startup decode-graph pre-capture" ("Description") turns such a wedge into a
+ * loud failure with a watchdog and reports which peers never arrived.  Here
+ * every device-side wait is bounded by the channel's timeout_us watchdog; a
+ * kernel that hits it, or sees the abort word, records the status in a
+ * host-mapped word and leaves `out` unwritten, and every later call on the
+ * channel returns that status without launching, so the failure cannot be
+ * missed or cascade through a replayed graph.
+ *
+ * ch: a channel from hr_create_channel.  Reads the host-mapped word; it does
+ * not synchronise, so synchronise the rank streams first to see the outcome
+ * of work already enqueued.  Recovery from an error is hr_destroy followed
+ * by hr_create_channel.
+ * Errors: HR_ERR_INVALID_ARG for a null channel.
  */
 HR_API hr_status hr_channel_status(hr_channel ch);
 
 /*
  * hr_channel_abort -- ask every kernel of this channel that is waiting, or
  * will wait, for its peer to stop: waits end with HR_ERR_ABORTED recorded in
- * the channel and `out` unwritten.  A wait reads the abort word once it has
- * lasted 20 us (polling it sooner slows every call), so a kernel stops within
- * microseconds of that.  Host-side store only; returns at once.
+ * the channel and `out` unwritten.
+ *
+ * The openinfer page ("Description") aborts loudly rather than letting a
+ * rank that spins on a peer hang the process; this is the host's handle on
+ * the same decision, for a caller that knows a peer will never arrive (a
+ * rank that failed, a shutdown) and does not want to wait for the watchdog.
+ * A wait reads the abort word once it has lasted 20 us (polling it sooner
+ * slows every call), so a kernel stops within microseconds of that.  The
+ * abort is sticky: the channel then refuses every call (hr_channel_status).
+ *
+ * ch: a channel from hr_create_channel.  Host-side store only; returns at
+ * once.  Errors: HR_ERR_INVALID_ARG for a null channel.
  */
 HR_API hr_status hr_channel_abort(hr_channel ch);
 
@@ -363,11 +396,23 @@ HR_API hr_status hr_channel_abort(hr_channel ch);
 HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *info);
 
 /*
- * hr_destroy -- release the channel.  Destroy any graph that captured calls
- * on it first, then synchronise the rank streams, then call this.  It
- * synchronises the channel's whole device before freeing the host memory the
- * kernels use, so it also waits for other work there (another channel's
- * waits end at the latest at that channel's watchdog).  NULL is a no-op.
+ * hr_destroy -- release the channel: its pinned host slots, flags, error and
+ * abort words, and its device call counters.
+ *
+ * Order of teardown.  The openinfer page ("Description") destroys captured
+ * graphs before the communicator they reference, and the SGLang pull request
+ * "[SM120] Add optional FlashInfer PCIe-IPC all-reduce for switch-free hosts"
+ * (review thread on its destroy() method) releases the all-reduce workspace
+ * before the process groups it uses.  Here: destroy every graph that
+ * captured calls on the channel, then synchronise the rank streams, then
+ * call this.  It synchronises the channel's whole device before freeing the
+ * host memory the kernels use, so it also waits for other work there
+ * (another channel's waits end at the latest at that channel's watchdog).
+ *
+ * ch: the channel, or NULL (a no-op returning HR_OK).  The handle is invalid
+ * afterwards, even when an error is returned.
+ * Errors: HR_ERR_HIP when the device synchronisation fails (the memory is
+ * released all the same).
  */
 HR_API hr_status hr_destroy(hr_channel ch);
 

@@ -344,7 +344,16 @@ class Channel:
                                         algorithm, link_mbps)
 
     def allreduce(self, rank: int, inp, out, stream=None):
-        """One rank's call; torch.float16 or torch.bfloat16 tensors."""
+        """One rank's call; torch.float16 or torch.bfloat16 tensors.
+
+        In loopback every rank's call must be in flight at once, on streams
+        from ``LoopbackStreams``.  Those streams are ordered with the null
+        stream (they are not non-blocking), so work on the null stream --
+        torch's default stream included -- enqueued between the ranks'
+        calls of one all-reduce holds back the ranks launched after it while
+        the others spin: the call ends at the channel's watchdog with the
+        sticky HR_ERR_TIMEOUT.  Enqueue nothing on the null stream between
+        the ranks' calls, or use ``allreduce_group``."""
         import torch
         n = inp.numel()
         if out.numel() != n:
