@@ -3,25 +3,29 @@
 
 Headline (the JSON line's ``value``): the two-rank exchange through pinned
 host slots at 32 tokens x hidden 4096 = 131072 binary16 values (256 KiB) per
-rank, both ranks on one GPU (loopback), each rank's K calls captured into
-its own hipGraph and replayed together.  One step = one all-reduce call of
-both ranks.  ``value`` is algorithmic GB/s = (G + 1) * N * 2 bytes per call
-over the per-call time (G = 2); the roofline peak of this path is the
+rank, both ranks on one GPU (loopback).  Each rank's 1000 back-to-back calls
+are captured into its own hipGraph; one step is one replay of both graphs
+(1000 all-reduce calls), ``--steps`` replays are timed after ``--warmup``
+untimed ones.  ``value`` is algorithmic GB/s = (G + 1) * N * 2 bytes per
+call over the per-call time (G = 2); the roofline peak of this path is the
 host-link bandwidth measured in the same run by a pinned hipMemcpy probe.
 
-Also reported in the same line (``configs``): every workload's us/call,
-GB/s and fraction of its roofline -- the two-rank fold with planted specials
-in HBM, the exchange at 1..32 tokens eager and graph-captured, the eight-rank
-decode-sized and prefill-sized folds in HBM (cold and warm cache), and the
-graph of 1000 exchange calls with fresh inputs per call -- plus the host-link
-probe and the CPU oracle timed on this host's cores.
+The last stdout line is one compact JSON object (a few KB): the headline,
+its roofline, the eight-rank prefill-size fold's HBM roofline, the CPU
+oracle baseline and a short table of every workload's us/call and fraction
+of its roofline.  The full per-workload results -- the two-rank fold with
+planted specials in HBM, the exchange at 1..32 tokens eager and
+graph-captured under every algorithm, groups of 4 and 8 ranks, the
+eight-rank decode-sized and prefill-sized folds in HBM (cold and warm
+cache), the graph of 1000 exchange calls with fresh inputs per call,
+bfloat16, the host-link probe -- go to the file named by ``--dump``.
 
 Every timed output is checked bit for bit (NaN by class) against torch's own
 binary16 adds on the device (a library cross-check; parity with the CPU
 oracle is the test suite's job).  Only the CPU-baseline leg runs the oracle:
 it times it and checks the headline's GPU output against it.
 
-Usage: python bench.py [--steps K] [--warmup W] [--quick] [--no-cpu]
+Usage: python bench.py [--steps K] [--warmup W] [--quick] [--no-cpu] [--dump FILE]
 """
 from __future__ import annotations
 
@@ -45,6 +49,11 @@ HIDDEN = 4096
 # device-side hold before timed back-to-back folds: longer than the host
 # takes to queue 50 launches through the binding (about 1 ms)
 FOLD_GATE_MS = 5.0
+# all-reduce calls per rank captured in the headline graph; one step is one
+# replay of both ranks' graphs
+CALLS_PER_STEP = 1000
+# largest size of the compact stdout line
+LINE_MAX_BYTES = 4096
 
 
 def log(msg):
@@ -54,8 +63,11 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2000, help="timed calls (one graph replay)")
-    p.add_argument("--warmup", type=int, default=200, help="untimed eager calls")
+    p.add_argument("--steps", type=int, default=20,
+                   help=f"timed steps: replays of both ranks' {CALLS_PER_STEP}-call graphs")
+    p.add_argument("--warmup", type=int, default=3, help="untimed replays before the timed ones")
+    p.add_argument("--dump", default=os.path.join(ROOT, "gpurun_out", "bench_full.json"),
+                   help="file that receives the full per-workload results")
     p.add_argument("--tokens", type=int, default=32)
     p.add_argument("--quick", action="store_true", help="headline only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
@@ -204,10 +216,10 @@ def capture_calls(c: Ctx, ch, rank, xin, out, stream, calls):
     return g
 
 
-def replay_all(c: Ctx, graphs, streams, gate_ms):
-    """Replay every rank's graph behind a common device-side gate; returns
-    (elapsed seconds on the GPU from gate open to all graphs done, host
-    submission seconds)."""
+def replay_all(c: Ctx, graphs, streams, gate_ms, replays=1):
+    """Replay every rank's graph `replays` times behind a common device-side
+    gate; returns (elapsed seconds on the GPU from gate open to all graphs
+    done, host submission seconds)."""
     torch = c.torch
     torch.cuda.synchronize()
     gate = c.gate(gate_ms)
@@ -216,9 +228,10 @@ def replay_all(c: Ctx, graphs, streams, gate_ms):
     e0, e1 = c.event(), c.event()
     e0.record(streams[0])
     t_host = time.perf_counter()
-    for g, st in zip(graphs, streams):
-        with torch.cuda.stream(st):
-            g.replay()
+    for _ in range(replays):
+        for g, st in zip(graphs, streams):
+            with torch.cuda.stream(st):
+                g.replay()
     t_host = time.perf_counter() - t_host
     for st in streams[1:]:
         ev = torch.cuda.Event()
@@ -256,7 +269,9 @@ ALGO_NAMES = {1: "one-shot", 2: "two-shot", 3: "low-latency"}
 
 
 def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=200, gate_ms=None,
-                      world=2, algorithm=0):
+                      world=2, algorithm=0, replays=1, warm_replays=2):
+    """`steps` calls per rank captured in one graph per rank; `warmup` eager
+    calls, then `warm_replays` untimed replays, then `replays` timed ones."""
     torch, hr, inputs = c.torch, c.hr, c.inputs
     xb = inputs.workload2(tokens) if world == 2 else inputs.workload6(world, tokens)
     n = xb[0].size
@@ -276,13 +291,13 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
         t_eager = eager_calls(c, ch, x, o, streams, eager_calls_n)
         graphs = [capture_calls(c, ch, r, x[r], o[r], streams[r], steps) for r in range(world)]
         if gate_ms is None:
-            gate_ms = 5.0 + steps * 0.01 * world / 2
-        for _ in range(2):                       # upload + settle, untimed
+            gate_ms = 5.0 + steps * replays * 0.01 * world / 2
+        for _ in range(max(warm_replays, 1)):    # upload + settle, untimed
             replay_all(c, graphs, streams, gate_ms)
         for t in o:
             t.zero_()
         torch.cuda.synchronize()
-        elapsed, host_s = replay_all(c, graphs, streams, gate_ms)
+        elapsed, host_s = replay_all(c, graphs, streams, gate_ms, replays)
         if ch.status() != hr.HR_OK:
             raise RuntimeError(f"exchange failed: {hr.hr_status_str(ch.status())}")
         got0 = c.to_host(o[0])
@@ -291,7 +306,7 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
         torch.cuda.synchronize()
     finally:
         ch.destroy()
-    t_graph = elapsed / steps
+    t_graph = elapsed / (steps * replays)
     alg = (world + 1) * n * 2
     two = taken == hr.HR_ALGO_TWO_SHOT
     if two:
@@ -311,7 +326,8 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
         "link_busiest_dir_frac": round(max(d2h, h2d) / t_graph / 1e9 / link_peak, 4),
         "eager_us": round(t_eager * 1e6, 3), "eager_GBps": round(alg / t_eager / 1e9, 2),
         "eager_frac_link": round(alg / t_eager / 1e9 / link_peak, 4),
-        "graph_calls": steps, "gate_ms": gate_ms, "host_submit_ms": round(host_s * 1e3, 3),
+        "graph_calls": steps, "replays": replays, "gate_ms": gate_ms,
+        "host_submit_ms": round(host_s * 1e3, 3),
         "gate_covered_submit": host_s * 1e3 < gate_ms,
         "bit_exact": exact,
         "_elapsed_s": elapsed,
@@ -691,8 +707,10 @@ def cpu_baseline(c: Ctx, tokens, gpu_out):
         calls += 1
         if time.perf_counter() - t0 > 1.5 and calls >= 3:
             break
-    t = (time.perf_counter() - t0) / calls
-    res["all"] = {"us_per_call": t * 1e6, "GBps": alg / t / 1e9, "cores": used, "calls": calls}
+    wall = time.perf_counter() - t0
+    t = wall / calls
+    res["all"] = {"us_per_call": t * 1e6, "GBps": alg / t / 1e9, "cores": used, "calls": calls,
+                  "wall_s": wall}
     calls, t0 = 0, time.perf_counter()
     while True:
         oracle.fold([x0b, x1b])
@@ -850,9 +868,10 @@ def main():
     probe, link_peak = host_link_probe(c)
     cfgs["host_link_probe"] = probe
 
-    log(f"headline: exchange graph, tokens={args.tokens}, K={args.steps}")
-    head = exchange_workload(c, args.tokens, args.steps, args.warmup, link_peak,
-                             gate_ms=args.gate_ms)
+    log(f"headline: exchange graphs of {CALLS_PER_STEP} calls, tokens={args.tokens}, "
+        f"{args.warmup} untimed + {args.steps} timed replays")
+    head = exchange_workload(c, args.tokens, CALLS_PER_STEP, 200, link_peak, gate_ms=args.gate_ms,
+                             replays=args.steps, warm_replays=args.warmup)
     elapsed = head.pop("_elapsed_s")
     head_out = head.pop("_out")
 
@@ -922,68 +941,160 @@ def main():
         cpu = cpu_baseline(c, args.tokens, head_out)
 
     c.destroy_streams()
-    t_call = elapsed / args.steps
+    full = {
+        "args": {"steps": args.steps, "warmup": args.warmup, "tokens": args.tokens,
+                 "quick": args.quick, "only": args.only},
+        "elapsed_s": elapsed, "link_peak": link_peak, "headline": head, "configs": cfgs,
+        "cpu": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "hip": torch.version.hip, "torch": torch.__version__},
+        "host": {"cpu": cpu_model(), "cores": len(os.sched_getaffinity(0))},
+        "traffic": {"exchange": measured_traffic("exchange_k<2,true,F16>"),
+                    "fold": measured_traffic("fold_vec<8,4,F16>")},
+    }
+    dump = args.dump
+    try:
+        os.makedirs(os.path.dirname(os.path.abspath(dump)), exist_ok=True)
+        with open(dump, "w") as f:
+            json.dump(full, f, indent=1, default=str)
+        log(f"full results: {dump}")
+    except OSError as e:
+        log(f"full results not written ({e})")
+        dump = None
+    print(json.dumps(make_line(full, dump), separators=(",", ":")), flush=True)
+
+
+def _r(x, nd=3):
+    return None if x is None else round(float(x), nd)
+
+
+def summary_table(full):
+    """Short per-workload table: name -> [us per call, fraction of roofline]
+    (the host link P for the exchange, 8 TB/s for the folds)."""
+    cfgs, t = full["configs"], {}
+    for r in cfgs.get("exchange_2rank_host_slots", []):
+        if r.get("auto"):
+            t[f"C2_{r['tokens']}tok_graph"] = [_r(r["graph_us"], 2), _r(r["graph_frac_link"])]
+    for r in cfgs.get("exchange_2rank_host_slots", []):
+        if r["tokens"] == 1 and not r.get("auto") and r["algorithm"] == "one-shot":
+            t["C2_1tok_one_shot_graph"] = [_r(r["graph_us"], 2), _r(r["graph_frac_link"])]
+    for key, name in (("fold_G2_N4096_specials", "C1_fold_G2_N4096_graph"),
+                      ("fold_G8_N393216", "C3_fold_G8_N393216_graph")):
+        if key in cfgs:
+            t[name] = [_r(cfgs[key]["graph_us"], 2), _r(cfgs[key]["graph_frac_hbm"])]
+    f4 = cfgs.get("fold_G8_N16777216")
+    if f4:
+        for k, name in (("cold_workspace", "C4_fold_cold_workspace"),
+                        ("cold_workspace_graph", "C4_fold_cold_workspace_graph"),
+                        ("cold", "C4_fold_cold_separate"), ("cold_graph", "C4_fold_cold_separate_graph"),
+                        ("warm", "C4_fold_warm_separate"), ("cold_single", "C4_fold_single_after_flush")):
+            if k + "_us" in f4:
+                t[name] = [_r(f4[k + "_us"], 2), _r(f4[k + "_frac_hbm"])]
+    for key, name in (("exchange_graph_1000_calls_N10240", "C5_graph1000"),
+                      ("exchange_graph_1000_calls_N10240_one_shot", "C5_graph1000_one_shot")):
+        if key in cfgs:
+            t[name] = [_r(cfgs[key]["us_per_call"], 2), _r(cfgs[key]["frac_link"])]
+    if "fold_graph_node_floor" in cfgs:
+        t["graph_node_floor"] = [_r(cfgs["fold_graph_node_floor"]["graph_us"], 2), None]
+    for r in cfgs.get("exchange_2rank_prefill", []):
+        if r["paced"] and r["algorithm"] == "one-shot":
+            t[f"exchange_2rank_{r['MiB_per_rank']:g}MiB_graph"] = [_r(r["graph_us"], 1),
+                                                                   _r(r["graph_frac_link"])]
+    for r in cfgs.get("exchange_group_launch_host_slots", []):
+        if r["world"] in (4, 8) and r["tokens"] in (1, 32) and r["algorithm"] == "two-shot":
+            t.setdefault(f"group_W{r['world']}_{r['tokens']}tok_two_shot",
+                         [_r(r["graph_us"], 2), _r(r["graph_frac_link"])])
+    b = cfgs.get("bf16", {})
+    if "fold_G8_N16777216_workspace" in b:
+        x = b["fold_G8_N16777216_workspace"]
+        t["bf16_C4_fold_cold_workspace"] = [_r(x["cold_us"], 2), _r(x["cold_frac_hbm"])]
+    if "exchange_2rank_256KiB_graph" in b:
+        x = b["exchange_2rank_256KiB_graph"]
+        t["bf16_C2_32tok_graph"] = [_r(x["us"], 2), _r(x["frac_link"])]
+    return t
+
+
+def all_bit_exact(obj):
+    """False when any result anywhere in `obj` has bit_exact false."""
+    if isinstance(obj, dict):
+        if obj.get("bit_exact") is False:
+            return False
+        return all(all_bit_exact(v) for v in obj.values())
+    if isinstance(obj, list):
+        return all(all_bit_exact(v) for v in obj)
+    return True
+
+
+def make_line(full, dump=None):
+    """The compact JSON line bench.py ends with (at most LINE_MAX_BYTES)."""
+    head, args, peak = full["headline"], full["args"], full["link_peak"]
+    calls = args["steps"] * CALLS_PER_STEP
+    t_call = full["elapsed_s"] / calls
     n = head["N"]
     alg = 3 * n * 2
     achieved = alg / t_call / 1e9
+    traffic = full["traffic"]["exchange"]
+    # the method's least traffic per rank launch: read the own input once,
+    # write the own slot, read the peer's slot, write the output
+    method_min = 4 * n * 2
     line = {
         "metric": METRIC,
         "value": round(achieved, 3),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(t_call * 1e3, 6),
+        "steps": args["steps"],
+        "warmup": args["warmup"],
+        "ms_per_step": round(full["elapsed_s"] / args["steps"] * 1e3, 4),
         "us_per_call": round(t_call * 1e6, 3),
+        "calls_per_step": CALLS_PER_STEP,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic: seeded N(0, 0.5^2) binary16 per rank",
-        "config": {"workload": "two-rank FP16 all-reduce through pinned host slots, loopback on "
-                               "one GPU, graph-captured",
-                   "G": 2, "tokens": args.tokens, "hidden": HIDDEN, "N": n,
-                   "bytes_per_call": alg, "calls_per_graph": args.steps,
-                   "parallelism": "none (one GPU; two ranks as two co-resident launches)"},
-        "roofline": {"bound": "host-link", "achieved": round(achieved, 3), "peak": link_peak,
-                     "unit": "GB/s", "frac": round(achieved / link_peak, 4),
-                     "traffic": measured_traffic("exchange_k<2,true,F16>"),
-                     "traffic_unit": "bytes per rank launch: FETCH_SIZE (scaled by a plain copy) "
-                                     "+ WRITE_SIZE, HBM and host bytes together",
+        "config": {"workload": "two-rank FP16 all-reduce through pinned host slots, 32 tokens x "
+                               "hidden 4096 (256 KiB per rank), loopback on one GPU, graph of "
+                               f"{CALLS_PER_STEP} calls per rank",
+                   "G": 2, "tokens": args["tokens"], "hidden": HIDDEN, "N": n, "bytes_per_call": alg,
+                   "algorithm": head["algorithm"], "parallelism": "none (one GPU; two ranks as two "
+                                                                  "co-resident launches)"},
+        "roofline": {"bound": "host-link", "achieved": round(achieved, 3), "peak": peak, "unit": "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "hr::exchange_k<2, true, hr::F16>",
+                     "kernel_avg_us": round(t_call * 1e6, 3),
+                     "busiest_dir_GBps": head["link_GBps_per_dir"],
+                     "busiest_dir_frac": head["link_busiest_dir_frac"],
+                     "traffic_over_method_min": None if traffic is None else round(traffic / method_min, 4),
                      "peak_source": "pinned hipMemcpyAsync probe, max(H2D, D2H) at 64 MiB, this run",
-                     "link_GBps_per_dir": head["link_GBps_per_dir"]},
-        "bit_exact": head["bit_exact"],
-        "headline": head,
-        "configs": cfgs,
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "hip": torch.version.hip, "torch": torch.__version__},
-        "host": {"cpu": cpu_model(), "cores": len(os.sched_getaffinity(0))},
+                     "traffic_unit": "bytes per rank launch (FETCH_SIZE x copy scale + WRITE_SIZE)"},
+        "bit_exact": head["bit_exact"] and all_bit_exact(full["configs"]),
     }
-    if "fold_G8_N16777216" in cfgs:
-        f4 = cfgs["fold_G8_N16777216"]
+    f4 = full["configs"].get("fold_G8_N16777216")
+    if f4:
         line["roofline_hbm_fold"] = {
             "bound": "hbm", "kernel": "hr::fold_vec<8, 4, hr::F16>", "G": 8, "N": f4["N"],
             "achieved": f4["cold_workspace_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": f4["cold_workspace_frac_hbm"],
-            "protocol": "3 rotating workspaces (contributions hr_workspace_stride apart), back-to-back",
-            "separate_allocations_frac": f4["cold_frac_hbm"], "warm_frac": f4["warm_frac_hbm"],
-            "single_launch_frac": f4["cold_single_frac_hbm"],
-            "traffic": measured_traffic("fold_vec<8,4,F16>"),
-            "traffic_unit": "bytes per launch: FETCH_SIZE (scaled by a plain copy) + WRITE_SIZE",
+            "frac": f4["cold_workspace_frac_hbm"], "kernel_avg_us": f4["cold_workspace_us"],
+            "traffic": full["traffic"]["fold"],
+            "protocol": "3 rotating workspaces (hr_workspace_stride layout), back-to-back",
+            "graph_frac": f4.get("cold_workspace_graph_frac_hbm"),
+            "separate_allocations_frac": f4.get("cold_frac_hbm"),
         }
+    cpu = full.get("cpu")
     if cpu is not None:
         line["cpu_baseline"] = {
             "value": round(cpu["all"]["GBps"], 4), "unit": "GB/s", "cores": cpu["all"]["cores"],
             "kind": "oracle",
-            "sample": f"the headline's two {n}-value contributions folded by the C oracle "
-                      f"{cpu['all']['calls']} times (~1.5 s wall) on all cores",
+            "sample": f"the headline's two {n}-value contributions folded {cpu['all']['calls']} "
+                      f"times by the C oracle on all cores (~{cpu['all']['wall_s']:.0f} s wall)",
             "us_per_call": round(cpu["all"]["us_per_call"], 2),
+            "one_core_us_per_call": round(cpu["one"]["us_per_call"], 2),
             "gpu_headline_matches_oracle": cpu["gpu_matches_oracle"],
-            "one_core": {"us_per_call": round(cpu["one"]["us_per_call"], 2),
-                         "GBps": round(cpu["one"]["GBps"], 4), "calls": cpu["one"]["calls"]},
         }
-    print(json.dumps(line), flush=True)
+    line["table_us_frac"] = summary_table(full)
+    line["host"] = f"{full['host']['cores']} cores, {full['host']['cpu']}"[:60]
+    line["full_results"] = None if dump is None else os.path.relpath(dump, ROOT)
+    return line
 
 
 if __name__ == "__main__":
