@@ -258,6 +258,42 @@ __device__ __forceinline__ uint64_t next_call(const ExchArgs &a, int b) {
     return s_epoch;
 }
 
+// Low-latency words carry only the low 32 bits of the call number, so a
+// word left in a slot 2^32 calls earlier would look current.  Each parity
+// of a rank's own LL slot is therefore cleared once every 2^31 call numbers:
+// at calls whose low 31 bits are 2 (even parity) or 3 (odd parity) -- the
+// second and third calls of a channel, and then every 2^31 -- every launched
+// workgroup of the rank zeroes its share of slot[e & 1][rank], except the
+// first `keep` units, which an LL call e writes itself.  A reader at LL call
+// e then finds in a peer's slot only zeros (never a call number: no call
+// number has zero low 32 bits) or words of calls in [c, e], c the peer's
+// last clearing of that parity before e, which finished before e started
+// (as in the parity argument above) and is less than 2^31 earlier, so no
+// word of a call other than e carries e's low 32 bits.  Nobody reads the
+// slot meanwhile: peers at call c read only units below keep, and every
+// peer finished its call c - 2 before this rank started call c.
+__device__ __forceinline__ bool ll_clear_due(uint64_t e) {
+    const uint32_t l = static_cast<uint32_t>(e) & 0x7FFFFFFFu;
+    return l == 2u || l == 3u;
+}
+
+__device__ __forceinline__ void ll_clear(const ExchArgs &a, int b, uint64_t e, size_t keep) {
+    const size_t half = a.ll_stride / 2;  // units per slot
+    if (keep >= half) return;
+    const size_t n = half - keep;
+    const size_t lo = keep + n * static_cast<size_t>(b) / static_cast<size_t>(a.nblocks);
+    const size_t hi = keep + n * static_cast<size_t>(b + 1) / static_cast<size_t>(a.nblocks);
+    const int parity = static_cast<int>(e & 1u);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        a.ll + static_cast<size_t>(a.world * parity + a.rank) * a.ll_stride, 0,
+        static_cast<int>(a.ll_stride * 16), kRawBufferDword3);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (size_t u = lo + threadIdx.x; u < hi; u += kExchThreads) {
+        __builtin_amdgcn_raw_buffer_store_b128(zero, r, static_cast<int>(u * 16), 0, kSysCoherent);
+        __builtin_amdgcn_raw_buffer_store_b128(zero, r, static_cast<int>((half + u) * 16), 0, kSysCoherent);
+    }
+}
+
 // Loads and stores share one counter on this GPU (vmcnt), and the compiler
 // cannot wait for a load with a partial count once a store is outstanding
 // too, so in these bounds-checked batch loops each host store waits for the
@@ -323,7 +359,9 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
     load_batch<T>(in, ulo + tid, uhi, active, x);
 
     const uint64_t e = next_call(a, b);
-    if (e == 0 || !active) return;
+    if (e == 0) return;
+    if (ll_clear_due(e)) ll_clear(a, b, e, 0);
+    if (!active) return;
     const int parity = static_cast<int>(e & 1u);
     const int rank = a.rank;
     __amdgpu_buffer_rsrc_t slot[W];
@@ -430,7 +468,9 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
     load_batch<T>(in, ulo + tid, uhi, active, x);
 
     const uint64_t e = next_call(a, b);
-    if (e == 0 || !active) return;
+    if (e == 0) return;
+    if (ll_clear_due(e)) ll_clear(a, b, e, 0);
+    if (!active) return;
     const int parity = static_cast<int>(e & 1u);
     const int rank = a.rank;
     __amdgpu_buffer_rsrc_t slot[W];
@@ -536,8 +576,9 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
 // then polls the two words of that unit in every peer's slot (all peers at
 // once) until every word carries e; after a barrier the workgroup folds left
 // in rank order and stores, or, if any lane of it timed out or saw an abort,
-// stores nothing.  A word of an earlier use of the parity holds e - 2, never
-// e; parity safety is the one-shot's argument, with "flag" read as "word".
+// stores nothing.  No word of an earlier call carries e's low 32 bits (see
+// ll_clear); parity safety is the one-shot's argument, with "flag" read as
+// "word".
 constexpr size_t kLLMaxNumel = 32768;      // values per call the LL slots hold
 // Largest call the automatic choice gives LL: its doubled bytes and its
 // readers polling every peer's data cost more as the group grows.  Measured
@@ -595,7 +636,9 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
     }
 
     const uint64_t e64 = next_call(a, b);  // its barrier also orders s_status's reset
-    if (e64 == 0 || !active) return;
+    if (e64 == 0) return;
+    if (ll_clear_due(e64)) ll_clear(a, b, e64, nunits);
+    if (!active) return;
     const uint32_t e = static_cast<uint32_t>(e64);  // the words carry the low 32 bits (never 0)
     const int parity = static_cast<int>(e64 & 1u);
     const int rank = a.rank;

@@ -588,3 +588,190 @@ def test_channel_at_the_size_limit(streams, algorithm):
     finally:
         torch.cuda.synchronize()
         ch.destroy()
+
+
+# ---------------------------------------------------------------- stale values
+#
+# Slots are double buffered by call parity (the 1Cat-vLLM page, "Purpose"):
+# a flag or a low-latency word left by an earlier call must never release a
+# waiter.  The host plays rank 1 and leaves values of earlier calls where a
+# waiter of call e looks; the kernel of rank 0 must not take them, so it ends
+# at its own short watchdog with `out` unwritten.  The same setup with the
+# current call number then completes, on a fresh channel.
+
+STALE_START = 1000          # counters before the call: the call number is 1001
+
+
+def _peer_flags(info, value):
+    for b in range(info.num_blocks):
+        info.host_flags[(1 * info.num_blocks + b) * info.flag_stride] = value
+
+
+def _peer_ll_words(info, bits, call, tag):
+    slot_bytes = info.ll_stride * 16
+    img, _ = ll_words(bits, tag, info.ll_stride // 2)
+    ctypes.memmove(info.host_ll + (2 * (call & 1) + 1) * slot_bytes, img.ctypes.data, img.nbytes)
+
+
+@pytest.mark.parametrize("stale", [1, 2], ids=["e-1", "e-2"])
+@pytest.mark.parametrize("algorithm", [hr.HR_ALGO_ONE_SHOT, hr.HR_ALGO_LL], ids=["one-shot", "ll"])
+def test_stale_peer_values_do_not_release(streams, algorithm, stale):
+    n = 4096
+    x0b, x1b = specials_mix(n, 51), specials_mix(n, 52)
+    x0 = to_dev(x0b)
+    e = _next_call_number(STALE_START)
+    # the peer's values are in place, but marked with call e - stale
+    ch = hr.Channel(timeout_us=20_000, algorithm=algorithm)
+    try:
+        info = ch.info()
+        _counters(ch, STALE_START)
+        out = torch.full_like(x0, 3.0)
+        if algorithm == hr.HR_ALGO_LL:
+            _peer_ll_words(info, x1b, e, e - stale)
+        else:
+            peer_slot = info.host_slots + (2 * (e & 1) + 1) * info.slot_stride * 2
+            ctypes.memmove(peer_slot, x1b.ctypes.data, n * 2)
+            _peer_flags(info, e - stale)
+        torch.cuda.synchronize()
+        say(f"stale peer values: algorithm {algorithm}, call {e}, peer marked {e - stale}")
+        ch.allreduce(0, x0, out, streams[0])
+        streams[0].synchronize()
+        assert ch.status() == hr.HR_ERR_TIMEOUT
+        assert torch.all(out == 3.0), "a stale value released the waiter"
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+    # the current call number releases the same wait
+    ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=algorithm)
+    try:
+        info = ch.info()
+        _counters(ch, STALE_START)
+        out = torch.full_like(x0, 3.0)
+        if algorithm == hr.HR_ALGO_LL:
+            _peer_ll_words(info, x1b, e, e)
+        else:
+            peer_slot = info.host_slots + (2 * (e & 1) + 1) * info.slot_stride * 2
+            ctypes.memmove(peer_slot, x1b.ctypes.data, n * 2)
+            _peer_flags(info, e)
+        torch.cuda.synchronize()
+        ch.allreduce(0, x0, out, streams[0])
+        streams[0].synchronize()
+        assert ch.status() == hr.HR_OK
+        assert_same_bits(to_host(out), oracle.add(x0b, x1b), "current call number")
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+
+
+def _ll_slot(info, parity, rank):
+    slot_bytes = info.ll_stride * 16
+    raw = ctypes.string_at(info.host_ll + (info.world_size * parity + rank) * slot_bytes, slot_bytes)
+    return np.frombuffer(raw, dtype=np.uint32).reshape(2, info.ll_stride // 2, 4).copy()
+
+
+def _plant_ll(info, parity, rank, tag):
+    """Every word of slot[parity][rank] set to {0x3c003c00, tag, 0x3c003c00, tag}:
+    values 1.0, call field `tag`, as a call of that number would leave them."""
+    half = info.ll_stride // 2
+    img = np.zeros((2, half, 4), np.uint32)
+    img[:, :, 0] = img[:, :, 2] = 0x3C003C00
+    img[:, :, 1] = img[:, :, 3] = tag & 0xFFFFFFFF
+    slot_bytes = info.ll_stride * 16
+    ctypes.memmove(info.host_ll + (info.world_size * parity + rank) * slot_bytes, img.ctypes.data,
+                   img.nbytes)
+
+
+@pytest.mark.parametrize("first", [hr.HR_ALGO_LL, hr.HR_ALGO_ONE_SHOT], ids=["ll", "one-shot"])
+def test_ll_clearing_removes_words_of_calls_2_32_earlier(streams, first):
+    """Low-latency words carry the low 32 bits of the call number.  Words
+    planted in both ranks' even-parity slots with the low 32 bits of call
+    c + 2 stand for words left by call c + 2 - 2^32 that no later call
+    overwrote.  Call c = 2^31 + 2 is a clearing point of the even parity: both
+    ranks zero their slot there except the units the call itself writes.  So
+    afterwards rank 0 alone at call c + 2 finds nothing to take and ends at
+    its watchdog with `out` unwritten.  At a call that is not a clearing
+    point (c + 4) the planted words stay, which shows the planting is what
+    a reader would see."""
+    c = (1 << 31) + 2
+    ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=first)
+    small = 8                                   # one 8-value unit
+    try:
+        info = ch.info()
+        half = info.ll_stride // 2
+        _counters(ch, c - 1)
+        for r in range(2):
+            _plant_ll(info, 0, r, c + 2)
+        # calls c and c + 1 of both ranks, `small` values each
+        for call in range(2):
+            x0b, x1b = specials_mix(small, 60 + call), specials_mix(small, 70 + call)
+            x0, x1 = to_dev(x0b), to_dev(x1b)
+            out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+            say(f"ll clearing: call {c + call}, first algorithm {first}")
+            loopback(ch, x0, x1, out0, out1, streams)
+            check_pair(out0, out1, x0b, x1b, f"call {c + call}")
+        keep = 1 if first == hr.HR_ALGO_LL else 0
+        for r in range(2):
+            slot = _ll_slot(info, 0, r)
+            assert not slot[:, keep:].any(), f"rank {r}: planted words survived the clearing call"
+            if keep:
+                assert (slot[:, 0, 1] == c).all() and (slot[:, 0, 3] == c).all()
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+
+    # rank 0 alone at call c + 2 on a channel in the same state
+    ch = hr.Channel(timeout_us=20_000, algorithm=hr.HR_ALGO_LL)
+    try:
+        info = ch.info()
+        _counters(ch, c - 1)
+        for r in range(2):
+            _plant_ll(info, 0, r, c + 2)
+        for call in range(2):
+            x0b, x1b = specials_mix(small, 60 + call), specials_mix(small, 70 + call)
+            x0, x1 = to_dev(x0b), to_dev(x1b)
+            loopback(ch, x0, x1, torch.empty_like(x0), torch.empty_like(x1), streams)
+        x = to_dev(specials_mix(4096, 80))
+        out = torch.full_like(x, 3.0)
+        torch.cuda.synchronize()
+        say(f"ll clearing: rank 0 alone at call {c + 2}")
+        ch.allreduce(0, x, out, streams[0])
+        streams[0].synchronize()
+        assert ch.status() == hr.HR_ERR_TIMEOUT
+        assert torch.all(out == 3.0), "a word of an earlier call released the reader"
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+
+    # control: no clearing at c + 2 (even, not a clearing point) -- the
+    # planted words that this call does not write stay in place
+    ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_LL)
+    try:
+        info = ch.info()
+        _counters(ch, c + 1)
+        for r in range(2):
+            _plant_ll(info, 0, r, c + 4)
+        x0b, x1b = specials_mix(small, 90), specials_mix(small, 91)
+        x0, x1 = to_dev(x0b), to_dev(x1b)
+        out0, out1 = torch.empty_like(x0), torch.empty_like(x1)
+        loopback(ch, x0, x1, out0, out1, streams)
+        check_pair(out0, out1, x0b, x1b, f"call {c + 2}")
+        for r in range(2):
+            slot = _ll_slot(info, 0, r)
+            assert (slot[:, 1:, 1] == ((c + 4) & 0xFFFFFFFF)).all()
+            assert (slot[:, 0, 1] == c + 2).all()
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+
+
+def test_loopback_streams_are_not_non_blocking(streams):
+    """hr.h states that a loopback stream is ordered with the null stream
+    (HIP creates a compute-unit-mask stream without hipStreamNonBlocking);
+    the runtime's own flags say so."""
+    hip = _hip_runtime()
+    hip.hipStreamGetFlags.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint)]
+    for s in streams:
+        flags = ctypes.c_uint(0xFFFF)
+        assert hip.hipStreamGetFlags(ctypes.c_void_p(s.cuda_stream), ctypes.byref(flags)) == 0
+        say(f"loopback stream flags: {flags.value:#x}")
+        assert flags.value & 1 == 0       # hipStreamNonBlocking is 0x1

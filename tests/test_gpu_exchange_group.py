@@ -44,7 +44,11 @@ def check_all(outs, xbits, what, bf16=False):
 
 
 @pytest.fixture(params=[(2, "auto"), (2, "one"), (2, "two"), (2, "ll"),
-                        (3, "one"), (4, "auto"), (4, "two"), (4, "ll"),
+                        (3, "auto"), (3, "one"), (3, "two"), (3, "ll"),
+                        (4, "auto"), (4, "two"), (4, "ll"),
+                        (5, "auto"), (5, "one"), (5, "two"), (5, "ll"),
+                        (6, "auto"), (6, "one"), (6, "two"), (6, "ll"),
+                        (7, "auto"), (7, "one"), (7, "two"), (7, "ll"),
                         (8, "auto"), (8, "one"), (8, "two"), (8, "ll")],
                 ids=lambda p: f"W{p[0]}-{p[1]}")
 def channel(request):

@@ -1,4 +1,4 @@
-"""GPU parity of hr_allreduce_f16 for groups of W = 3..8 ranks.
+"""GPU parity of hr_allreduce_f16 for groups of W = 3..8 ranks (every size).
 
 All W ranks run on one GPU as concurrently resident launches on W streams
 that each own a hardware queue (loopback).  Every rank's output must equal,
@@ -49,9 +49,10 @@ def check_all(outs, xbits, what):
 ALGOS = {"one": hr.HR_ALGO_ONE_SHOT, "two": hr.HR_ALGO_TWO_SHOT, "ll": hr.HR_ALGO_LL}
 
 
-@pytest.fixture(params=[(3, "one"), (4, "one"), (8, "one"),
-                        (2, "two"), (3, "two"), (4, "two"), (8, "two"),
-                        (3, "ll"), (4, "ll"), (8, "ll")],
+@pytest.fixture(params=[(3, "one"), (4, "one"), (5, "one"), (6, "one"), (7, "one"), (8, "one"),
+                        (2, "two"), (3, "two"), (4, "two"), (5, "two"), (6, "two"), (7, "two"),
+                        (8, "two"),
+                        (3, "ll"), (4, "ll"), (5, "ll"), (6, "ll"), (7, "ll"), (8, "ll")],
                 ids=lambda p: f"W{p[0]}-{p[1]}")
 def group(request):
     W, algo = request.param
