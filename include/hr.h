@@ -353,6 +353,49 @@ HR_API hr_status hr_allreduce_group_bf16(hr_channel ch, const void *const *ins, 
                                          hr_stream_t stream);
 
 /*
+ * hr_allreduce_group_noalloc_f16 -- hr_allreduce_group_f16 for callers that
+ * cannot allocate: code under hipGraph capture before any channel exists,
+ * tight serving loops, harnesses that forbid hipMalloc.  It needs no channel
+ * and allocates nothing: the state a channel would allocate (slots, flags,
+ * call counters, error words) lives in a fixed device array inside the
+ * library, HR_NOALLOC_SCRATCH_BYTES per device, which each device that the
+ * library runs on holds until the process ends.  Its slots are in device
+ * memory (HBM), not pinned host memory: the exchange protocol, the kernels
+ * and the result bits are those of hr_allreduce_group_f16 under
+ * HR_ALGO_AUTO, the left fold of ins[0..W-1] in rank order into every
+ * outs[r].
+ *
+ * Enqueues two kernels on `stream`: a small fill that clears the array's
+ * flags, counters and error words (and, for a low-latency call, the words
+ * that call reads), then the group exchange.  So every call starts from a
+ * cleared state and leaves the array holding its own contents; nothing
+ * carries from one call to the next.  Calls that overlap on one device --
+ * on different streams, or in different threads at once -- share the array
+ * and race; calls on one stream do not.  The first call on a device looks up
+ * the array's device address (once, under a lock); make that first call
+ * outside any capture.
+ *
+ * ins, outs:  world_size device binary16 buffers of numel values each, as
+ *             for hr_allreduce_group_f16 (outs[r] == ins[r] allowed, any
+ *             other overlap with a rank's buffers an error); the arrays are
+ *             copied into the launch.
+ * world_size: 2..HR_MAX_WORLD.
+ * numel:      at most HR_NOALLOC_MAX_NUMEL; 0 enqueues nothing.
+ * status:     NULL, or a 4-byte aligned device word that the fill sets to
+ *             HR_OK and the exchange to HR_ERR_TIMEOUT if a wait exceeds the
+ *             default watchdog (a launch that cannot be resident at once,
+ *             because other work fills the device); `outs` is then unwritten.
+ * Errors (synchronous, nothing enqueued): HR_ERR_UNSUPPORTED (world_size out
+ * of range, or a device whose compute-unit count needs more than the
+ * array), HR_ERR_TOO_LARGE (numel above HR_NOALLOC_MAX_NUMEL),
+ * HR_ERR_INVALID_ARG, HR_ERR_ALIGNMENT, HR_ERR_HIP.
+ */
+#define HR_NOALLOC_MAX_NUMEL 131072u
+#define HR_NOALLOC_SCRATCH_BYTES (8u << 20)
+HR_API hr_status hr_allreduce_group_noalloc_f16(const void *const *ins, void *const *outs, int world_size,
+                                                size_t numel, uint32_t *status, hr_stream_t stream);
+
+/*
  * hr_channel_status -- the channel's sticky asynchronous status: HR_OK, or
  * HR_ERR_TIMEOUT / HR_ERR_ABORTED once a kernel has recorded one.
  *

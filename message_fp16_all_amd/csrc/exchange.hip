@@ -76,6 +76,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <type_traits>
 #include <vector>
@@ -1356,4 +1357,201 @@ extern "C" HR_API hr_status hr_loopback_stream_create(int device, hr_stream_t *o
 extern "C" HR_API hr_status hr_loopback_stream_destroy(hr_stream_t stream) {
     if (stream == nullptr) return HR_OK;
     return hipStreamDestroy(reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? HR_OK : HR_ERR_HIP;
+}
+
+// ------------------------------------------------- allocation-free group call
+//
+// hr_allreduce_group_noalloc_f16 runs the loopback group call without a
+// channel: the state a channel allocates at creation (slots, reduced-shard
+// slots, flags, low-latency words, call counters, error and abort words) sits
+// in `scratch`, one array per device that lives as long as the process.  The
+// array is device memory, so the slots are in HBM rather than in pinned host
+// memory; the kernels are the group kernels above, unchanged (their
+// system-coherent accesses are coherent on device memory too), and the fold
+// and its bits are the same.  The layout is that of a channel of
+// kNoAllocMaxNumel values, computed per call from the group size and the
+// device's workgroup count.
+//
+// Every call starts from a zeroed state: a fill kernel on the call's stream
+// clears the flags, the call counters, the error words and (for a
+// low-latency call) the low-latency words the call reads, so the call's
+// number is 1 and no value of an earlier call can release a wait.  The fill
+// uses system-coherent stores, like every other access to this state, so the
+// exchange kernel's system-coherent loads see the zeros.  Calls that overlap
+// on one device share the array and race; calls on one stream do not.
+
+constexpr size_t kNoAllocMaxNumel = HR_NOALLOC_MAX_NUMEL;
+constexpr size_t kNoAllocBytes = HR_NOALLOC_SCRATCH_BYTES;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+struct NoAllocLayout {
+    size_t stride, ll_stride;
+    size_t slots, reduced, flags, flags2, ll, epochs, dev_error, host_error, abort_w, total;
+};
+
+inline NoAllocLayout noalloc_layout(int world, int nb) {
+    NoAllocLayout L{};
+    L.stride = round_up(kNoAllocMaxNumel, kLine / sizeof(uint16_t));
+    const size_t ll_max = kNoAllocMaxNumel < kLLMaxNumel ? kNoAllocMaxNumel : kLLMaxNumel;
+    L.ll_stride = 2 * ((ll_max + kVecElems - 1) / kVecElems);
+    const size_t flag_bytes = static_cast<size_t>(world) * static_cast<size_t>(nb) * kLine;
+    L.slots = 0;
+    L.reduced = round_up(2 * static_cast<size_t>(world) * L.stride * sizeof(uint16_t), kLine);
+    L.flags = L.reduced + round_up(2 * L.stride * sizeof(uint16_t), kLine);
+    L.flags2 = L.flags + flag_bytes;
+    L.ll = L.flags2 + flag_bytes;
+    L.epochs = L.ll + round_up(2 * static_cast<size_t>(world) * L.ll_stride * sizeof(u32x4), kLine);
+    L.dev_error = L.epochs + round_up(static_cast<size_t>(world) * nb * sizeof(uint64_t), kLine);
+    L.host_error = L.dev_error + kLine;
+    L.abort_w = L.host_error + kLine;
+    L.total = L.abort_w + kLine;
+    return L;
+}
+
+// Up to three ranges of 16-byte units and one 32-bit word, zeroed with
+// system-coherent stores; workgroups stride over the units of each range.
+struct NoAllocClear {
+    u32x4 *base[3];
+    uint32_t units[3];
+    uint32_t *word;
+};
+
+__global__ __launch_bounds__(kExchThreads) void noalloc_clear_k(NoAllocClear c) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const uint32_t step = gridDim.x * kExchThreads;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        if (c.units[k] == 0) continue;
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(c.base[k], 0, static_cast<int>(c.units[k] * 16), kRawBufferDword3);
+        for (uint32_t u = blockIdx.x * kExchThreads + threadIdx.x; u < c.units[k]; u += step)
+            __builtin_amdgcn_raw_buffer_store_b128(zero, r, static_cast<int>(u * 16), 0, kSysCoherent);
+    }
+    if (c.word != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        __hip_atomic_store(c.word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+namespace {
+
+// The device address of `scratch` on each device (host code never uses the
+// array's own name: on the host it only stands for the symbol), with the
+// device's wall-clock rate; looked up once per device, on its first call.
+struct NoAllocDevice {
+    unsigned char *ptr = nullptr;
+    int clock_khz = 0;
+};
+NoAllocDevice g_noalloc[64];
+std::mutex g_noalloc_mu;
+
+hipError_t noalloc_device(int dev, NoAllocDevice *out) {
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    NoAllocDevice &d = g_noalloc[dev];
+    if (d.ptr == nullptr) {
+        DeviceGuard guard(dev);
+        if (!guard.ok) return hipErrorInvalidDevice;
+        int clock_khz = 0;
+        hipError_t e = hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev);
+        if (e != hipSuccess) return e;
+        if (clock_khz <= 0) return hipErrorInvalidValue;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        d.clock_khz = clock_khz;
+        d.ptr = static_cast<unsigned char *>(p);
+    }
+    *out = d;
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" HR_API hr_status hr_allreduce_group_noalloc_f16(const void *const *ins, void *const *outs, int world_size,
+                                                           size_t numel, uint32_t *status, hr_stream_t stream) {
+    if (world_size < 2 || world_size > kMaxWorld) return HR_ERR_UNSUPPORTED;
+    if (numel == 0) return HR_OK;
+    if (ins == nullptr || outs == nullptr) return HR_ERR_INVALID_ARG;
+    if (numel > kNoAllocMaxNumel) return HR_ERR_TOO_LARGE;
+    if (status != nullptr && !aligned(status, 4)) return HR_ERR_ALIGNMENT;
+    const int W = world_size;
+    const size_t bytes = numel * 2;
+    bool vec = true;
+    for (int r = 0; r < W; ++r) {
+        if (ins[r] == nullptr || outs[r] == nullptr) return HR_ERR_INVALID_ARG;
+        if (!aligned(ins[r], 2) || !aligned(outs[r], 2)) return HR_ERR_ALIGNMENT;
+        vec = vec && aligned(ins[r], 16) && aligned(outs[r], 16);
+    }
+    for (int r = 0; r < W; ++r) {
+        if (partial_overlap(ins[r], outs[r], bytes)) return HR_ERR_INVALID_ARG;
+        for (int q = 0; q < W; ++q) {
+            if (q == r) continue;
+            if (ranges_overlap(outs[r], outs[q], bytes) || ranges_overlap(outs[r], ins[q], bytes))
+                return HR_ERR_INVALID_ARG;
+        }
+    }
+
+    int dev = -1, cus = 0;
+    if (stream_device(stream, &dev) != hipSuccess) return HR_ERR_HIP;
+    if (device_cu_count(dev, &cus) != hipSuccess) return HR_ERR_HIP;
+    int nb = cus / W;
+    if (nb < 1) nb = 1;
+    const NoAllocLayout L = noalloc_layout(W, nb);
+    if (L.total > kNoAllocBytes) return HR_ERR_UNSUPPORTED;  // a device with more compute units than planned for
+    NoAllocDevice d;
+    if (noalloc_device(dev, &d) != hipSuccess) return HR_ERR_HIP;
+    unsigned char *base = d.ptr;
+
+    const Algo algo = choose_algo(HR_ALGO_AUTO, numel, W, nb);
+    GroupArgs g{};
+    ExchArgs &a = g.a;
+    a.numel = numel;
+    a.slots = reinterpret_cast<uint16_t *>(base + L.slots);
+    a.stride = L.stride;
+    a.flags = reinterpret_cast<uint64_t *>(base + L.flags);
+    a.flags2 = reinterpret_cast<uint64_t *>(base + L.flags2);
+    a.reduced = reinterpret_cast<uint16_t *>(base + L.reduced);
+    a.ll = reinterpret_cast<u32x4 *>(base + L.ll);
+    a.ll_stride = L.ll_stride;
+    a.epochs = reinterpret_cast<uint64_t *>(base + L.epochs);
+    a.dev_error = reinterpret_cast<uint32_t *>(base + L.dev_error);
+    a.host_error = status != nullptr ? status : reinterpret_cast<uint32_t *>(base + L.host_error);
+    a.abort_w = reinterpret_cast<const uint32_t *>(base + L.abort_w);
+    a.timeout_ticks = static_cast<uint64_t>(HR_DEFAULT_TIMEOUT_US) * static_cast<uint64_t>(d.clock_khz) / 1000u;
+    a.abort_after_ticks = static_cast<uint64_t>(kAbortAfterUs) * static_cast<uint64_t>(d.clock_khz) / 1000u;
+    a.pace_q16 = 0;  // the slots are in HBM: no host link to pace for
+    a.rank = 0;
+    a.world = W;
+    a.nblocks = nb;
+    a.nactive = algo == Algo::two_shot ? active_blocks2(numel, nb, W)
+                : algo == Algo::ll     ? active_blocks_ll(numel)
+                                       : active_blocks(numel, nb, W);
+    for (int r = 0; r < W; ++r) {
+        g.in[r] = ins[r];
+        g.out[r] = outs[r];
+    }
+
+    // zero what the call's waits compare against: both flag arrays, the call
+    // counters through the abort word, and (LL) the parity-1 low-latency
+    // words of every rank -- the call number is 1
+    NoAllocClear c{};
+    c.base[0] = reinterpret_cast<u32x4 *>(base + L.flags);
+    c.units[0] = static_cast<uint32_t>((L.ll - L.flags) / sizeof(u32x4));
+    c.base[1] = reinterpret_cast<u32x4 *>(base + L.epochs);
+    c.units[1] = static_cast<uint32_t>((L.total - L.epochs) / sizeof(u32x4));
+    if (algo == Algo::ll) {
+        c.base[2] = reinterpret_cast<u32x4 *>(base + L.ll) + static_cast<size_t>(W) * L.ll_stride;
+        c.units[2] = static_cast<uint32_t>(static_cast<size_t>(W) * L.ll_stride);
+    }
+    c.word = status;
+    const uint32_t units = c.units[0] > c.units[2] ? c.units[0] : c.units[2];
+    uint32_t grid = (units + kExchThreads - 1) / kExchThreads;
+    if (grid > static_cast<uint32_t>(cus)) grid = static_cast<uint32_t>(cus);
+    if (grid < 1) grid = 1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(noalloc_clear_k, dim3(grid), dim3(kExchThreads), 0, s, c);
+    if (hipGetLastError() != hipSuccess) return HR_ERR_HIP;
+    launch_group_w<F16>(g, vec, algo, s);
+    return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
 }

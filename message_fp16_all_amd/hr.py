@@ -30,6 +30,8 @@ HR_MAX_G = 16
 HR_MAX_WORLD = 8
 HR_DEFAULT_MAX_NUMEL = 131072
 HR_MAX_NUMEL_LIMIT = 1 << 29
+HR_NOALLOC_MAX_NUMEL = 131072
+HR_NOALLOC_SCRATCH_BYTES = 8 << 20
 HR_DEFAULT_TIMEOUT_US = 1_000_000
 HR_DEFAULT_LINK_MBPS = 50_000
 HR_LINK_UNPACED = 0xFFFFFFFF
@@ -46,7 +48,7 @@ EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel
            "hr_loopback_stream_create", "hr_loopback_stream_destroy",
            "hr_reduce_bf16", "hr_allreduce_bf16", "hr_admit", "hr_route_str", "hr_decode_numel",
            "hr_workspace_stride", "hr_exchange_algorithm", "hr_allreduce_group_f16",
-           "hr_allreduce_group_bf16")
+           "hr_allreduce_group_bf16", "hr_allreduce_group_noalloc_f16")
 
 HR_ROUTE_HOST = 0
 HR_DECLINE_DISABLED = 1
@@ -129,6 +131,8 @@ def load() -> ctypes.CDLL:
     lib.hr_allreduce_bf16.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
     lib.hr_allreduce_group_f16.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_size_t, vp]
     lib.hr_allreduce_group_bf16.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_size_t, vp]
+    lib.hr_allreduce_group_noalloc_f16.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
+                                                   ctypes.c_size_t, vp, vp]
     lib.hr_reduce_bf16.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.hr_channel_status.argtypes = [vp]
     lib.hr_exchange_algorithm.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
@@ -203,6 +207,15 @@ def hr_allreduce_group_bf16(ch: int, in_ptrs, out_ptrs, numel: int, stream: int)
     ins = (ctypes.c_void_p * max(1, len(in_ptrs)))(*in_ptrs)
     outs = (ctypes.c_void_p * max(1, len(out_ptrs)))(*out_ptrs)
     return load().hr_allreduce_group_bf16(ch, ins, outs, numel, stream)
+
+
+def hr_allreduce_group_noalloc_f16(in_ptrs, out_ptrs, world_size: int, numel: int, status_ptr,
+                                   stream: int) -> int:
+    """Raw call of the channel-free group all-reduce; ``status_ptr`` is a
+    device address or None.  Returns the hr_status code."""
+    ins = (ctypes.c_void_p * max(1, len(in_ptrs)))(*in_ptrs)
+    outs = (ctypes.c_void_p * max(1, len(out_ptrs)))(*out_ptrs)
+    return load().hr_allreduce_group_noalloc_f16(ins, outs, world_size, numel, status_ptr, stream)
 
 
 def hr_reduce_bf16(ptrs, G: int, out_ptr: int, numel: int, stream: int) -> int:
@@ -331,6 +344,30 @@ def reduce(tensors, out, stream=None):
     fn, name = (hr_reduce_bf16, "hr_reduce_bf16") if bf else (hr_reduce_f16, "hr_reduce_f16")
     _check(fn(ptrs, len(ptrs), _f16_ptr(out, "out", dt), n, _stream_handle(stream, out)), name)
     return out
+
+
+def allreduce_group_noalloc(ins, outs, status=None, stream=None):
+    """Every rank's call in one launch without a channel
+    (hr_allreduce_group_noalloc_f16): ``ins[r]``/``outs[r]`` are rank r's
+    torch.float16 tensors; ``status``, if given, a one-element torch.int32
+    (or uint32) device tensor that receives the call's status."""
+    W = len(ins)
+    if len(outs) != W:
+        raise ValueError("ins and outs differ in length")
+    n = ins[0].numel()
+    for r in range(W):
+        if ins[r].numel() != n or outs[r].numel() != n:
+            raise ValueError(f"rank {r}: every input and output must hold {n} values")
+    ip = [_f16_ptr(t, f"ins[{r}]") for r, t in enumerate(ins)]
+    op = [_f16_ptr(t, f"outs[{r}]") for r, t in enumerate(outs)]
+    sp = None
+    if status is not None:
+        if status.numel() < 1 or status.element_size() != 4 or not status.is_cuda:
+            raise TypeError("status: expected a 4-byte device tensor")
+        sp = status.data_ptr()
+    _check(hr_allreduce_group_noalloc_f16(ip, op, W, n, sp, _stream_handle(stream, outs[0])),
+           "hr_allreduce_group_noalloc_f16")
+    return outs
 
 
 class Channel:

@@ -129,3 +129,20 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(hr, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         hr.load()
+
+
+def test_noalloc_group_validation_before_any_device_call():
+    f = hr.hr_allreduce_group_noalloc_f16
+    two = [FAKE, FAKE + 65536]
+    outs = [FAKE + 2 * 65536, FAKE + 3 * 65536]
+    for ws in (0, 1, 9):
+        assert f(two, outs, ws, 16, None, 0) == hr.HR_ERR_UNSUPPORTED
+    assert f(two, outs, 2, 0, None, 0) == hr.HR_OK                              # empty: no-op
+    assert f(two, outs, 2, hr.HR_NOALLOC_MAX_NUMEL + 1, None, 0) == hr.HR_ERR_TOO_LARGE
+    assert f([FAKE, 0], outs, 2, 16, None, 0) == hr.HR_ERR_INVALID_ARG          # null input
+    assert f(two, [outs[0], FAKE + 1], 2, 16, None, 0) == hr.HR_ERR_ALIGNMENT
+    assert f(two, outs, 2, 16, FAKE + 2, 0) == hr.HR_ERR_ALIGNMENT              # status word
+    assert f(two, [outs[0], outs[0] + 8], 2, 16, None, 0) == hr.HR_ERR_INVALID_ARG  # outputs overlap
+    assert f(two, [two[1], outs[1]], 2, 16, None, 0) == hr.HR_ERR_INVALID_ARG   # out 0 is rank 1's input
+    lib = hr.load()
+    assert lib.hr_allreduce_group_noalloc_f16(None, None, 2, 16, None, None) == hr.HR_ERR_INVALID_ARG
