@@ -33,15 +33,17 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into ``message_fp16_all_amd/libhr.so``."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def build(verbose: bool = False, defines=(), lib: str = LIB) -> str:
+    """Compile every source into ``lib`` (``message_fp16_all_amd/libhr.so``
+    by default); ``defines`` are extra preprocessor macros (the diagnostic
+    timeline build uses HR_TIMELINE)."""
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(f"-D{d}" for d in defines), *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -60,8 +60,9 @@
 //      that lasts over 20 us also reads the abort word, and a watchdog on
 //      the constant-rate wall clock bounds the wait
 //   4. barrier, then system-coherent loads of slot[e & 1][q] for every
-//      peer q (H2D) and plain loads of its own slice of `in` again; store
-//      the left fold x0 + x1 + ... + x_{W-1}, in rank order, to `out`.
+//      peer q (H2D) and its own values (still in registers when the slice
+//      gave each lane one unit, else loaded from `in` again); store the left
+//      fold x0 + x1 + ... + x_{W-1}, in rank order, to `out`.
 // Why one parity cannot be overwritten while a peer still reads it: a rank
 // starts call e + 2 (same parity as e) only after its call e + 1 has
 // finished, and in call e + 1 its workgroup 0 (always active) waited for
@@ -119,6 +120,36 @@ template <class E>
 __device__ __forceinline__ u32x4 combine(u32x4 x0, u32x4 x1) { return E::add8(x0, x1); }
 template <class E>
 __device__ __forceinline__ uint16_t combine(uint16_t x0, uint16_t x1) { return E::add1(x0, x1); }
+
+// Timeline instrumentation, compiled only into the diagnostic library that
+// message_fp16_all_amd/timeline.py builds with -DHR_TIMELINE: lane 0 of
+// every workgroup keeps wall-clock stamps of its protocol phases and writes
+// them, with its poll count, to record ((e - 1) mod calls, rank, workgroup)
+// of a device buffer the tool attaches.  In the library itself HR_NOW() is a
+// constant and tl_record is empty, so none of it is compiled in.
+#ifdef HR_TIMELINE
+constexpr int kTimelineWords = 8;  // stamps t0..t5, count, call number
+__device__ uint64_t *hr_tl_buf;
+__device__ uint64_t hr_tl_calls;
+#define HR_NOW() static_cast<uint64_t>(wall_clock64())
+#define HR_COUNT(x) (++(x))
+#else
+#define HR_NOW() uint64_t(0)
+#define HR_COUNT(x) ((void)0)
+#endif
+
+__device__ __forceinline__ void tl_record(const ExchArgs &a, int b, uint64_t e, uint64_t t0, uint64_t t1,
+                                          uint64_t t2, uint64_t t3, uint64_t t4, uint64_t t5, uint64_t count) {
+#ifdef HR_TIMELINE
+    if (threadIdx.x != 0 || hr_tl_buf == nullptr || hr_tl_calls == 0) return;
+    const size_t rec = static_cast<size_t>((e - 1) % hr_tl_calls) * a.world * a.nblocks +
+                       static_cast<size_t>(a.rank) * a.nblocks + static_cast<size_t>(b);
+    uint64_t *p = hr_tl_buf + rec * kTimelineWords;
+    p[0] = t0; p[1] = t1; p[2] = t2; p[3] = t3; p[4] = t4; p[5] = t5; p[6] = count; p[7] = e;
+#else
+    (void)a; (void)b; (void)e; (void)t0; (void)t1; (void)t2; (void)t3; (void)t4; (void)t5; (void)count;
+#endif
+}
 
 // The combine takes one 16-byte unit per lane per step (W loads in flight
 // per lane).  Reads of host memory lose rate when too many are in flight at
@@ -356,6 +387,7 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
     // the first batch of this lane's values is loaded before the call
     // counter and the pacing wait, so its HBM latency overlaps them
     constexpr size_t kBatch = static_cast<size_t>(kExchThreads) * kExchUnroll;
+    const uint64_t tl0 = HR_NOW();
     T x[kExchUnroll];
     load_batch<T>(in, ulo + tid, uhi, active, x);
 
@@ -363,6 +395,7 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
     if (e == 0) return;
     if (ll_clear_due(e)) ll_clear(a, b, e, 0);
     if (!active) return;
+    const uint64_t tl1 = HR_NOW();
     const int parity = static_cast<int>(e & 1u);
     const int rank = a.rank;
     __amdgpu_buffer_rsrc_t slot[W];
@@ -373,6 +406,7 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
     // 1. publish this rank's slice into its host slot (write-through),
     //    paced so that each workgroup's handshake and reads start early
     pace(a, b, (hi - lo) * 16u * W);
+    const uint64_t tl2 = HR_NOW();
     for (size_t v0 = ulo + tid;;) {
         store_batch<T>(slot[rank], v0, uhi, x);
         v0 += kBatch;
@@ -389,6 +423,7 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
     if (tid == 0)
         __hip_atomic_store(a.flags + (static_cast<size_t>(rank) * a.nblocks + b) * kFlagStride, e,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint64_t tl3 = HR_NOW();
 
     // 3. the first wave waits for every peer's flag, one lane per peer
     if (tid < 64) {
@@ -399,15 +434,19 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
     // wave saw; the loads themselves read host memory, not a cached copy
     __syncthreads();
     if (s_status != 0) return;
+    const uint64_t tl4 = HR_NOW();
 
-    // 4. combine: left fold in rank order x0 + x1 + ... + x_{W-1}
+    // 4. combine: left fold in rank order x0 + x1 + ... + x_{W-1}; when the
+    //    slice gave every lane at most one unit, the lane's own unit is
+    //    still in x[0] from the publish and is not read from `in` again
+    const bool one_unit = uhi - ulo <= static_cast<size_t>(kExchThreads);
     for (size_t v = ulo + tid; v < uhi; v += kExchThreads) {
-        T x[W];
+        T xs[W];
 #pragma unroll
-        for (int q = 0; q < W; ++q) x[q] = (q == rank) ? in[v] : HostIO<T>::load(slot[q], v);
-        T acc = x[0];
+        for (int q = 0; q < W; ++q) xs[q] = (q == rank) ? (one_unit ? x[0] : in[v]) : HostIO<T>::load(slot[q], v);
+        T acc = xs[0];
 #pragma unroll
-        for (int q = 1; q < W; ++q) acc = combine<E>(acc, x[q]);
+        for (int q = 1; q < W; ++q) acc = combine<E>(acc, xs[q]);
         out[v] = acc;
     }
     if (last && tail0 + tid < a.numel) {
@@ -420,6 +459,8 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
         }
         static_cast<uint16_t *>(a.out)[i] = acc;
     }
+    // timeline: entry, counter, pace done, flag raised, peers seen, combined
+    tl_record(a, b, e, tl0, tl1, tl2, tl3, tl4, HR_NOW(), 0);
 }
 
 // Two-shot variant for larger payloads and groups: the active workgroups
@@ -504,13 +545,15 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
         }
         __syncthreads();
         if (s_status != 0) return;
+        const bool one_unit = uhi - ulo <= static_cast<size_t>(kExchThreads);  // own unit still in x[0]
         for (size_t v = ulo + tid; v < uhi; v += kExchThreads) {
-            T x[W];
+            T xs[W];
 #pragma unroll
-            for (int q = 0; q < W; ++q) x[q] = (q == rank) ? in[v] : HostIO<T>::load(slot[q], v);
-            T acc = x[0];
+            for (int q = 0; q < W; ++q)
+                xs[q] = (q == rank) ? (one_unit ? x[0] : in[v]) : HostIO<T>::load(slot[q], v);
+            T acc = xs[0];
 #pragma unroll
-            for (int q = 1; q < W; ++q) acc = combine<E>(acc, x[q]);
+            for (int q = 1; q < W; ++q) acc = combine<E>(acc, xs[q]);
             out[v] = acc;
             HostIO<T>::store(red, v, acc);
         }
@@ -619,6 +662,7 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
     const size_t u = lo + static_cast<size_t>(tid);
     const bool has = active && u < hi;
     const uint16_t *in16 = static_cast<const uint16_t *>(a.in);
+    const uint64_t tl0 = HR_NOW();
 
     // this lane's unit of `in` (zero past numel), loaded before the call
     // counter so that its HBM latency overlaps the counter's
@@ -640,6 +684,7 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
     if (e64 == 0) return;
     if (ll_clear_due(e64)) ll_clear(a, b, e64, nunits);
     if (!active) return;
+    const uint64_t tl1 = HR_NOW();
     const uint32_t e = static_cast<uint32_t>(e64);  // the words carry the low 32 bits (never 0)
     const int parity = static_cast<int>(e64 & 1u);
     const int rank = a.rank;
@@ -661,6 +706,7 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
         __builtin_amdgcn_raw_buffer_store_b128(w0, ll[rank], off0, 0, kSysCoherent);
         __builtin_amdgcn_raw_buffer_store_b128(w1, ll[rank], off1, 0, kSysCoherent);
     }
+    const uint64_t tl2 = HR_NOW();
 
     // optionally hold the first poll until this lane's own words are
     // acknowledged (the peers wrote theirs at about the same time)
@@ -670,8 +716,10 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
     u32x4 got[W];
     unsigned pending = has ? (((1u << W) - 1u) & ~(1u << rank)) : 0u;
     uint32_t status = 0;
+    uint32_t polls = 0;
     const long long t0 = wall_clock64();
     for (;;) {
+        HR_COUNT(polls);
         // all pending peers' loads in flight at once
         u32x4 w0[W], w1[W];
 #pragma unroll
@@ -705,8 +753,10 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
         __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.host_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
+    const uint64_t tl3 = HR_NOW();
     __syncthreads();
     if (s_status != 0 || !has) return;
+    const uint64_t tl4 = HR_NOW();
 
     // left fold in rank order, own values from registers
     u32x4 acc = (rank == 0) ? x : got[0];
@@ -722,6 +772,9 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
             if (i < a.numel) out16[i] = static_cast<uint16_t>(acc[k / 2] >> (16 * (k % 2)));
         }
     }
+    // timeline: entry, counter, words issued, lane 0's words seen, workgroup's
+    // words seen, stored; lane 0's polls
+    tl_record(a, b, e64, tl0, tl1, tl2, tl3, tl4, HR_NOW(), polls);
 }
 
 // One launch per rank: workgroup b of the rank named in the arguments.
@@ -1555,3 +1608,14 @@ extern "C" HR_API hr_status hr_allreduce_group_noalloc_f16(const void *const *in
     launch_group_w<F16>(g, vec, algo, s);
     return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
 }
+
+#ifdef HR_TIMELINE
+// Diagnostic library only: attach the timeline buffer (records of
+// kTimelineWords 64-bit words, `calls` x world x num_blocks of them) on the
+// current device; NULL detaches.
+extern "C" HR_API hr_status hr_timeline_attach(void *buf, uint64_t calls) {
+    if (hipMemcpyToSymbol(HIP_SYMBOL(hr_tl_buf), &buf, sizeof(buf)) != hipSuccess) return HR_ERR_HIP;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(hr_tl_calls), &calls, sizeof(calls)) != hipSuccess) return HR_ERR_HIP;
+    return hipDeviceSynchronize() == hipSuccess ? HR_OK : HR_ERR_HIP;
+}
+#endif
