@@ -72,9 +72,16 @@ def parse():
     p.add_argument("--quick", action="store_true", help="headline only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--only", default="", help="comma list of sections: exchange,world,fold,c5,bf16")
-    p.add_argument("--profile-kernel", choices=("fold", "exchange", "copy"), default=None,
+    p.add_argument("--profile-kernel", choices=("fold", "fold-separate", "exchange", "copy", "link-probe"),
+                   default=None,
                    help="run one kernel --reps times and nothing else (for rocprofv3 counters)")
     p.add_argument("--reps", type=int, default=10)
+    p.add_argument("--num-blocks", type=int, default=0,
+                   help="workgroups per rank of the channel the exchange profiling target makes "
+                        "(0: the library's default)")
+    p.add_argument("--link-mbps", type=int, default=0,
+                   help="pacing rate of the channel the exchange profiling target makes (0: the "
+                        "library's default; 4294967295: unpaced)")
     p.add_argument("--gate-ms", type=float, default=None,
                    help="hold both rank streams this long before a timed replay (default "
                         "5 ms + 10 us per call; raise it under a profiler, which slows graph "
@@ -770,7 +777,7 @@ def measured_traffic(kernel):
 
 # ------------------------------------------------------- profiling targets
 
-def profile_kernel(which, reps):
+def profile_kernel(which, reps, link_mbps=0, num_blocks=0):
     """Launch one kernel `reps` times with nothing else timed, for
     rocprofv3 (counter collection serialises dispatches, so the exchange runs
     one rank against a peer that the host plays: the host writes the peer's
@@ -793,11 +800,26 @@ def profile_kernel(which, reps):
         torch.cuda.synchronize()
         log(f"copy: {reps} x 256 MiB")
         return
-    if which == "fold":
-        # the cold protocol of the timed run: launches cycle over three
-        # workspaces (864 MiB), so none finds its inputs in the MALL
+    if which == "link-probe":
+        # a channel that measures the host link at creation: its probe kernel
+        # (1 warm-up + 3 timed launches) reads 16 MiB of device memory and
+        # writes them to pinned host memory while it reads 16 MiB of pinned
+        # host memory -- known host-read bytes, to read the memory counters by
+        ch = hr.Channel(link_mbps=hr.HR_LINK_CALIBRATE)
+        log(f"link probe: {ch.info().link_mbps} MB/s")
+        ch.destroy()
+        return
+    if which in ("fold", "fold-separate"):
+        # the cold protocol of the timed run: launches cycle over three sets
+        # of inputs (864 MiB), so none finds its inputs in the MALL; the sets
+        # are workspaces (hr_workspace_stride layout) or, for fold-separate,
+        # separately allocated tensors
         xs = inputs.workload4()
-        wss = [hr.workspace(len(xs), xs[0].size) for _ in range(3)]
+        if which == "fold":
+            wss = [hr.workspace(len(xs), xs[0].size) for _ in range(3)]
+        else:
+            wss = [(None, [torch.empty(xs[0].size, dtype=torch.float16, device=dev) for _ in xs])
+                   for _ in range(3)]
         for _buf, ts in wss:
             for t, x in zip(ts, xs):
                 t.copy_(to_dev(x))
@@ -811,14 +833,15 @@ def profile_kernel(which, reps):
         for t in ts[1:]:
             acc = acc + t
         ok = all(bool(torch.equal(o.view(torch.int16), acc.view(torch.int16))) for o in outs[:min(reps, 3)])
-        log(f"fold G=8 N={xs[0].size}: {reps} launches over 3 rotating workspaces, bit_exact={ok}")
+        log(f"fold G=8 N={xs[0].size}: {reps} launches over 3 rotating "
+            f"{'workspaces' if which == 'fold' else 'sets of separate tensors'}, bit_exact={ok}")
         return
     x0b, x1b = inputs.workload2(32)
     n = x0b.size
     x0 = to_dev(x0b)
     out = torch.empty_like(x0)
     streams = hr.LoopbackStreams(0)
-    ch = hr.Channel(timeout_us=2_000_000)
+    ch = hr.Channel(timeout_us=2_000_000, link_mbps=link_mbps, num_blocks=num_blocks)
     info = ch.info()
     algo = ch.algorithm_for(n)
     if algo != hr.HR_ALGO_ONE_SHOT:
@@ -855,7 +878,7 @@ def main():
               f"(--gpus {args.gpus} requested); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.profile_kernel:
-        profile_kernel(args.profile_kernel, args.reps)
+        profile_kernel(args.profile_kernel, args.reps, args.link_mbps, args.num_blocks)
         return
     c = Ctx()
     torch = c.torch
@@ -1066,7 +1089,8 @@ def make_line(full, dump=None):
                      "busiest_dir_frac": head["link_busiest_dir_frac"],
                      "traffic_over_method_min": None if traffic is None else round(traffic / method_min, 4),
                      "peak_source": "pinned hipMemcpyAsync probe, max(H2D, D2H) at 64 MiB, this run",
-                     "traffic_unit": "bytes per rank launch (FETCH_SIZE x copy scale + WRITE_SIZE)"},
+                     "traffic_unit": "bytes per rank launch, HBM and host reads and writes (rocprofv3 "
+                                     "TCC_EA0 DRAM/IO 32-byte request counters, copy scale 1.0)"},
         "bit_exact": head["bit_exact"] and all_bit_exact(full["configs"]),
     }
     f4 = full["configs"].get("fold_G8_N16777216")

@@ -443,10 +443,12 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
     for (size_t v = ulo + tid; v < uhi; v += kExchThreads) {
         T xs[W];
 #pragma unroll
-        for (int q = 0; q < W; ++q) xs[q] = (q == rank) ? (one_unit ? x[0] : in[v]) : HostIO<T>::load(slot[q], v);
-        T acc = xs[0];
+        for (int q = 0; q < W; ++q)  // every peer's load issued before any is used
+            if (q != rank) xs[q] = HostIO<T>::load(slot[q], v);
+        const T own = one_unit ? x[0] : in[v];
+        T acc = rank == 0 ? own : xs[0];
 #pragma unroll
-        for (int q = 1; q < W; ++q) acc = combine<E>(acc, xs[q]);
+        for (int q = 1; q < W; ++q) acc = combine<E>(acc, q == rank ? own : xs[q]);
         out[v] = acc;
     }
     if (last && tail0 + tid < a.numel) {
@@ -550,10 +552,11 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
             T xs[W];
 #pragma unroll
             for (int q = 0; q < W; ++q)
-                xs[q] = (q == rank) ? (one_unit ? x[0] : in[v]) : HostIO<T>::load(slot[q], v);
-            T acc = xs[0];
+                if (q != rank) xs[q] = HostIO<T>::load(slot[q], v);
+            const T own = one_unit ? x[0] : in[v];
+            T acc = rank == 0 ? own : xs[0];
 #pragma unroll
-            for (int q = 1; q < W; ++q) acc = combine<E>(acc, xs[q]);
+            for (int q = 1; q < W; ++q) acc = combine<E>(acc, q == rank ? own : xs[q]);
             out[v] = acc;
             HostIO<T>::store(red, v, acc);
         }
