@@ -1,6 +1,6 @@
 """The built library's gfx950 kernels need no scratch memory.
 
-A kernel with a private segment (a call stack, spilled registers) makes the
+A kernel with a private segment (a call stack, spilled vector registers) makes the
 GPU set up scratch for every dispatch, which costs microseconds per launch --
 the exchange is a few-microsecond kernel, so that alone would show up as a
 large slowdown.  This reads the kernel descriptors' metadata from the code
@@ -59,8 +59,10 @@ def kernel_metadata(tmp_path):
 def test_no_kernel_uses_scratch(tmp_path):
     kernels = kernel_metadata(tmp_path)
     assert any("exchange_k" in k for k in kernels) and any("fold_vec" in k for k in kernels)
+    # a VGPR spill or a call stack needs scratch memory; an SGPR spill goes
+    # to a VGPR lane (and would show a private segment if it did not)
     bad = {k: v for k, v in kernels.items()
            if v.get("private_segment_fixed_size", "0") != "0"
            or v.get("uses_dynamic_stack", "false") != "false"
-           or v.get("vgpr_spill_count", "0") != "0" or v.get("sgpr_spill_count", "0") != "0"}
+           or v.get("vgpr_spill_count", "0") != "0"}
     assert not bad, f"kernels with scratch: {sorted(bad)[:5]}"
