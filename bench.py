@@ -487,6 +487,9 @@ def fold_time_warm(c: Ctx, ts, out, reps, gated=False):
 
 
 def fold_time_graph(c: Ctx, ts, out, calls):
+    """Per-launch time of a graph of `calls` folds; the stream is held behind
+    a device-side gate until the replay is queued, so the host's submission
+    of the graph is not timed."""
     torch, hr = c.torch, c.hr
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
@@ -497,6 +500,7 @@ def fold_time_graph(c: Ctx, ts, out, calls):
     torch.cuda.synchronize()
     e0, e1 = c.event(), c.event()
     cur = torch.cuda.current_stream()
+    cur.wait_event(c.gate(FOLD_GATE_MS))
     e0.record(cur)
     g.replay()
     e1.record(cur)
@@ -548,7 +552,8 @@ def fold_time_rotating(c: Ctx, sets, outs, reps=30):
 
 def fold_time_rotating_graph(c: Ctx, sets, outs, reps=30):
     """As fold_time_rotating, with the back-to-back launches captured in one
-    graph, so host submission cannot gap them."""
+    graph, so host submission cannot gap them; gated like it, so the host's
+    submission of the graph launch is not timed either."""
     torch, hr = c.torch, c.hr
     k = len(sets)
     s = torch.cuda.Stream()
@@ -563,6 +568,7 @@ def fold_time_rotating_graph(c: Ctx, sets, outs, reps=30):
     cur = torch.cuda.current_stream()
     for _ in range(3):
         e0, e1 = c.event(), c.event()
+        cur.wait_event(c.gate(FOLD_GATE_MS))
         e0.record(cur)
         g.replay()
         e1.record(cur)

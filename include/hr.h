@@ -96,8 +96,10 @@ typedef enum {
 #define HR_DEFAULT_TIMEOUT_US 1000000u
 
 /* Host-link rate the one-shot and the two-shot pace their workgroups by
-   (MB/s; see hr_channel_config.link_mbps): the default, the values that turn
-   pacing off and that measure the link, and the smallest rate accepted. */
+   (MB/s; see hr_channel_config.link_mbps): the rate taken when the library's
+   measurement fails (a PCIe 5.0 x16 link as measured on MI355X hosts, whose
+   one-way copies reach 55 GB/s), the values that turn pacing off and that
+   measure the link anew, and the smallest rate accepted. */
 #define HR_DEFAULT_LINK_MBPS 50000u
 #define HR_LINK_UNPACED 0xFFFFFFFFu
 #define HR_LINK_CALIBRATE 0xFFFFFFFEu /* measure the link at channel creation */
@@ -135,10 +137,13 @@ typedef struct {
     int algorithm;        /* HR_ALGO_*; 0 = automatic                         */
     uint32_t link_mbps;   /* rate (MB/s) at which the host link that the
                              channel's ranks share carries writes while
-                             reads run the other way; 0 =
-                             HR_DEFAULT_LINK_MBPS (a PCIe 5.0 x16 link as
-                             measured on MI355X hosts, whose one-way copies
-                             reach 55 GB/s).  The
+                             reads run the other way.  0 = measured: the
+                             first channel created with 0 on a device runs
+                             the HR_LINK_CALIBRATE measurement below and the
+                             library keeps the rate for every later such
+                             channel on that device, for the life of the
+                             process (HR_DEFAULT_LINK_MBPS if the
+                             measurement fails).  The
                              one-shot and the two-shot start workgroup b's
                              publish b - 2 slices later than workgroups
                              0..2's, a slice taking world_size x slice bytes
@@ -153,9 +158,12 @@ typedef struct {
                              hr_create_channel times a kernel that writes
                              16 MiB to pinned host memory while it reads
                              16 MiB from it (best of 3, after a warm-up) and
-                             paces by that rate; this takes a few
+                             paces 1/32 above that rate (measured best on
+                             MI355X hosts: slices start just before the
+                             link would run dry); this takes a few
                              milliseconds and should run while the link is
-                             otherwise idle.                                  */
+                             otherwise idle (so should the first channel
+                             created with 0 on a device).                     */
 } hr_channel_config;
 
 /* Read-only description of a channel, for diagnostics and tests. */

@@ -1050,12 +1050,12 @@ struct DeviceGuard {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// The rate (MB/s) at which the host link carries writes while reads run the
-// other way, which is what a paced exchange's publish meets: link_probe_k
-// moves kCalibBytes each way at once on stream `s` (best of kCalibReps after
-// one warm-up), with writers and readers in the proportion that moved the
-// most in a sweep on MI355X (128 and 64 workgroups).  At least
-// HR_MIN_LINK_MBPS; 0 when a HIP call fails.
+// The pacing rate (MB/s) for the host link: the rate at which it carries
+// writes while reads run the other way, which is what a paced exchange's
+// publish meets, plus 1/32.  link_probe_k moves kCalibBytes each way at once
+// on stream `s` (best of kCalibReps after one warm-up), with writers and
+// readers in the proportion that moved the most in a sweep on MI355X (128
+// and 64 workgroups).  At least HR_MIN_LINK_MBPS; 0 when a HIP call fails.
 uint32_t calibrate_link(hipStream_t s, int cus) {
     constexpr size_t kCalibBytes = size_t(16) << 20;
     constexpr int kCalibReps = 3;
@@ -1093,8 +1093,31 @@ uint32_t calibrate_link(hipStream_t s, int cus) {
     if (hrd != nullptr) (void)hipHostFree(hrd);
     if (hw != nullptr) (void)hipHostFree(hw);
     if (!ok || best <= 0.f) return 0;
-    const double mbps = static_cast<double>(kCalibBytes) / (static_cast<double>(best) * 1e-3) / 1e6;
+    // pace 1/32 above the measured rate: slices then start just before the
+    // link would run dry.  Measured on MI355X hosts (probe 48.4 GB/s), two
+    // ranks, graph-captured, by pacing rate 45 / 48 / 50 / 52 / 55 GB/s:
+    // 256 KiB 17.99 / 17.24 / 17.15 / 17.06 / 17.07 us, 1 MiB 53.5 / 51.1 /
+    // 50.3 / 51.8 / 53.4 us, 16 MiB 792 / 737 / 719 / 751 / 789 us; and the
+    // probe's own rate against 50 GB/s on one box: 17.05-17.46 against
+    // 16.93-17.32 us at 256 KiB, 734-739 against 725-734 us at 16 MiB.
+    const double mbps = static_cast<double>(kCalibBytes) / (static_cast<double>(best) * 1e-3) / 1e6 * 33.0 / 32.0;
     return mbps < HR_MIN_LINK_MBPS ? HR_MIN_LINK_MBPS : static_cast<uint32_t>(mbps);
+}
+
+// The rate a channel created with link_mbps = 0 paces by: measured once per
+// device (calibrate_link, on the first such channel) and kept for the
+// process; HR_DEFAULT_LINK_MBPS when the measurement fails.
+std::mutex g_link_mu;
+uint32_t g_link_mbps[64];
+
+uint32_t device_link_mbps(int dev, hipStream_t s, int cus) {
+    if (dev < 0 || dev >= 64) return HR_DEFAULT_LINK_MBPS;
+    std::lock_guard<std::mutex> lock(g_link_mu);
+    if (g_link_mbps[dev] == 0) {
+        const uint32_t m = calibrate_link(s, cus);
+        g_link_mbps[dev] = m != 0 ? m : HR_DEFAULT_LINK_MBPS;
+    }
+    return g_link_mbps[dev];
 }
 
 void release(hr_channel ch) {
@@ -1150,7 +1173,7 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->timeout_us = timeout_us;
     ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
     ch->abort_after_ticks = static_cast<uint64_t>(kAbortAfterUs) * static_cast<uint64_t>(clock_khz) / 1000u;
-    ch->link_mbps = cfg->link_mbps ? cfg->link_mbps : HR_DEFAULT_LINK_MBPS;
+    ch->link_mbps = cfg->link_mbps;  // 0: the device's measured rate, below
 
     const size_t slot_bytes = 2 * static_cast<size_t>(world) * ch->stride * sizeof(uint16_t);
     const size_t flag_bytes = static_cast<size_t>(world) * static_cast<size_t>(nb) * kLine;
@@ -1180,6 +1203,8 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     if (ok && ch->link_mbps == HR_LINK_CALIBRATE) {
         ch->link_mbps = calibrate_link(init, cus);
         ok = ch->link_mbps != 0;
+    } else if (ok && ch->link_mbps == 0) {
+        ch->link_mbps = device_link_mbps(cfg->device, init, cus);
     }
     if (init != nullptr) (void)hipStreamDestroy(init);
     if (!ok) {

@@ -525,12 +525,13 @@ def test_publish_pacing(streams, link_mbps, algorithm):
     ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=algorithm, link_mbps=link_mbps)
     try:
         got = ch.info().link_mbps
-        if link_mbps == hr.HR_LINK_CALIBRATE:
-            # a PCIe 5.0 x16 host link moves about 50-60 GB/s each way
-            say(f"calibrated host link: {got} MB/s")
+        if link_mbps in (hr.HR_LINK_CALIBRATE, 0):
+            # measured anew, or once per device for the default; a PCIe 5.0
+            # x16 host link moves about 50-60 GB/s each way
+            say(f"measured host link ({'anew' if link_mbps else 'default'}): {got} MB/s")
             assert 20_000 <= got <= 80_000
         else:
-            assert got == (hr.HR_DEFAULT_LINK_MBPS if link_mbps == 0 else link_mbps)
+            assert got == link_mbps
         for call, n in enumerate([131_072, 65_541, 4096]):
             x0b, x1b = specials_mix(n, seed=900 + call), specials_mix(n, seed=950 + call)
             x0, x1 = to_dev(x0b), to_dev(x1b)
@@ -775,3 +776,17 @@ def test_loopback_streams_are_not_non_blocking(streams):
         assert hip.hipStreamGetFlags(ctypes.c_void_p(s.cuda_stream), ctypes.byref(flags)) == 0
         say(f"loopback stream flags: {flags.value:#x}")
         assert flags.value & 1 == 0       # hipStreamNonBlocking is 0x1
+
+
+def test_default_rate_is_measured_once_per_device():
+    """Channels created with link_mbps = 0 all pace by one rate, measured
+    on the device by the first of them and kept by the library."""
+    rates = []
+    for _ in range(3):
+        ch = hr.Channel(timeout_us=TIMEOUT_US)
+        try:
+            rates.append(ch.info().link_mbps)
+        finally:
+            ch.destroy()
+    say(f"default pacing rates: {rates}")
+    assert len(set(rates)) == 1 and 20_000 <= rates[0] <= 80_000
