@@ -322,8 +322,10 @@ def exchange_workload(c: Ctx, tokens, steps, warmup, link_peak, eager_calls_n=20
     else:
         d2h = world * n * 2                 # each rank publishes its slice once
         h2d = world * (world - 1) * n * 2   # each rank reads every peer's slice
-        if taken == hr.HR_ALGO_LL:          # every 4 bytes of values travel with 4 of call number
-            d2h, h2d = 2 * d2h, 2 * h2d
+        if taken == hr.HR_ALGO_LL:          # every 6 bytes of values travel with 2 of call field
+            units = -(-n // 8)              # and a unit of 8 values takes three 8-byte words
+            d2h = world * units * 24
+            h2d = world * (world - 1) * units * 24
     return {
         "world": world, "algorithm": ALGO_NAMES[taken], "link_mbps": link_mbps,
         "tokens": tokens, "N": n, "bytes_per_call": alg,

@@ -117,9 +117,9 @@ typedef enum {
 #define HR_ALGO_TWO_SHOT 2  /* shard owners fold, then everyone gathers;
                                needs num_blocks >= world_size             */
 #define HR_ALGO_LL 3        /* low-latency one-shot: every 8-byte word in
-                               host memory carries 4 bytes of values and
-                               the call number, so readers poll the data
-                               itself (no flags); twice the link bytes; up
+                               host memory carries 6 bytes of values and a
+                               16-bit call field, so readers poll the data
+                               itself (no flags); 4/3 of the link bytes; up
                                to 32768 values (larger calls: one-shot)   */
 
 typedef struct {
@@ -189,12 +189,13 @@ typedef struct {
     volatile uint64_t *host_flags2; /* two-shot reduced-shard flags, laid out
                                      like host_flags                          */
     void *host_ll;                /* low-latency slots [2 parity][world]
-                                     [ll_stride] 16-byte words, each slot two
-                                     halves of ll_stride / 2 words; unit u of
-                                     a call is word u of the first half,
-                                     {v0v1, call, v2v3, call}, and word u of
-                                     the second, {v4v5, call, v6v7, call}     */
-    size_t ll_stride;             /* 16-byte words per low-latency slot       */
+                                     [ll_stride] 64-bit words, each slot three
+                                     planes of ll_stride / 3 words; unit u of
+                                     a call (values v0..v7) is word u of each
+                                     plane: v0 v1 v2, v3 v4 v5 and v6 v7 0 in
+                                     bits 0..47, the call field in bits 48..63
+                                     (the call number's low 15 bits | 0x8000) */
+    size_t ll_stride;             /* 64-bit words per low-latency slot        */
     uint32_t link_mbps;           /* the pacing rate in effect (MB/s), or
                                      HR_LINK_UNPACED                          */
     uint64_t *dev_epochs;         /* device address of the call counters
@@ -202,8 +203,8 @@ typedef struct {
                                      each rank's workgroup took.  Call numbers
                                      run 1, 2, 3, ... skipping every value
                                      whose low 32 bits are zero; a flag holds
-                                     the full number, a low-latency word its
-                                     low 32 bits.                             */
+                                     the full number, a low-latency word the
+                                     call field above.                        */
 } hr_channel_info;
 
 /*
@@ -234,9 +235,10 @@ HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out
  * shard in rank order and publish it, and every rank gather the others'
  * folded shards: less host-link traffic for W > 2, the same bits.  The
  * low-latency one-shot (HR_ALGO_LL, or automatic for small calls: up to
- * 12288 values for two ranks, fewer for larger groups) puts the call number into every 8-byte word it writes to host
- * memory, so a peer polls the values themselves: no flag, no wait for
- * acknowledgements, one host-link round trip less; the same bits again.
+ * 12288 values for two ranks, fewer for larger groups) puts a call field
+ * into every 8-byte word it writes to host memory, so a peer polls the
+ * values themselves: no flag, no wait for acknowledgements, one host-link
+ * round trip less; the same bits again.
  *
  * Enqueues exactly one kernel on `stream`.  Its workgroups each own one
  * contiguous slice of the numel values: they copy the slice of `in` into this

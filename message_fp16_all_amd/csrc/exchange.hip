@@ -101,8 +101,8 @@ struct ExchArgs {
     uint64_t *flags;          // device view of the host flags (publish)
     uint64_t *flags2;         // device view of the host flags (reduced shard, two-shot)
     uint16_t *reduced;        // device view of the reduced-shard slots [2][stride] (two-shot)
-    u32x4 *ll;                // device view of the low-latency slots [2][W][ll_stride] (LL)
-    size_t ll_stride;         // 16-byte words per low-latency slot
+    uint64_t *ll;             // device view of the low-latency slots [2][W][ll_stride] (LL)
+    size_t ll_stride;         // 8-byte words per low-latency slot: three planes of ll_stride / 3
     uint64_t *epochs;         // this rank's call counters (HBM)
     uint32_t *dev_error;      // HBM
     uint32_t *host_error;     // device view of the host error word
@@ -277,53 +277,64 @@ __device__ __forceinline__ void pace(const ExchArgs &a, int b, uint64_t slice_by
 // Advance this workgroup's call counter (every launched workgroup does, so a
 // rank's workgroups agree on the slot parity); returns the call number e, or
 // 0 when the channel already holds an error.
-__device__ __forceinline__ uint64_t next_call(const ExchArgs &a, int b) {
+// With commit false the caller stores the new number itself, later, with
+// commit_call: only workgroup b of this rank touches epochs[b], and the next
+// call on the rank starts after this kernel has ended, so the store may come
+// anywhere before the workgroup ends.
+__device__ __forceinline__ uint64_t next_call(const ExchArgs &a, int b, bool commit = true) {
     __shared__ uint64_t s_epoch;
     if (threadIdx.x == 0) {
         const uint32_t err = __hip_atomic_load(a.dev_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint64_t e =
             next_call_number(__hip_atomic_load(&a.epochs[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (err == 0) __hip_atomic_store(&a.epochs[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (err == 0 && commit) __hip_atomic_store(&a.epochs[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_epoch = err == 0 ? e : 0u;
     }
     __syncthreads();
     return s_epoch;
 }
 
-// Low-latency words carry only the low 32 bits of the call number, so a
-// word left in a slot 2^32 calls earlier would look current.  Each parity
-// of a rank's own LL slot is therefore cleared once every 2^31 call numbers:
-// at calls whose low 31 bits are 2 (even parity) or 3 (odd parity) -- the
-// second and third calls of a channel, and then every 2^31 -- every launched
-// workgroup of the rank zeroes its share of slot[e & 1][rank], except the
-// first `keep` units, which an LL call e writes itself.  A reader at LL call
-// e then finds in a peer's slot only zeros (never a call number: no call
-// number has zero low 32 bits) or words of calls in [c, e], c the peer's
-// last clearing of that parity before e, which finished before e started
-// (as in the parity argument above) and is less than 2^31 earlier, so no
-// word of a call other than e carries e's low 32 bits.  Nobody reads the
-// slot meanwhile: peers at call c read only units below keep, and every
-// peer finished its call c - 2 before this rank started call c.
+__device__ __forceinline__ void commit_call(const ExchArgs &a, int b, uint64_t e) {
+    if (threadIdx.x == 0) __hip_atomic_store(&a.epochs[b], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Low-latency words carry a 16-bit call field: the call number's low 15
+// bits with the top bit set, so it is never zero.  A word left in a slot
+// 2^15 call numbers earlier would look current, so each parity of a rank's
+// own LL slot is cleared once every 2^14 call numbers: at calls whose low 14
+// bits are 2 (even parity) or 3 (odd parity) -- the second and third calls
+// of a channel, and then every 2^14 -- every launched workgroup of the rank
+// zeroes its share of slot[e & 1][rank], except the first `keep` units,
+// which an LL call e writes itself.  A reader at LL call e then finds in a
+// peer's slot only zeros (no call field is zero) or words of calls in [c, e],
+// c the peer's last clearing of that parity before e, which finished before
+// e started (as in the parity argument above) and is less than 2^15 call
+// numbers earlier, so no word of a call other than e carries e's call field.
+// Nobody reads the slot meanwhile: peers at call c read only units below
+// keep, and every peer finished its call c - 2 before this rank started call
+// c.  A clearing call stores at most the slot (3 x 8 bytes per unit) once
+// more; at one call in 2^14 that costs nothing measurable.
 __device__ __forceinline__ bool ll_clear_due(uint64_t e) {
-    const uint32_t l = static_cast<uint32_t>(e) & 0x7FFFFFFFu;
+    const uint32_t l = static_cast<uint32_t>(e) & 0x3FFFu;
     return l == 2u || l == 3u;
 }
 
 __device__ __forceinline__ void ll_clear(const ExchArgs &a, int b, uint64_t e, size_t keep) {
-    const size_t half = a.ll_stride / 2;  // units per slot
-    if (keep >= half) return;
-    const size_t n = half - keep;
+    const size_t plane = a.ll_stride / 3;  // units per slot
+    if (keep >= plane) return;
+    const size_t n = plane - keep;
     const size_t lo = keep + n * static_cast<size_t>(b) / static_cast<size_t>(a.nblocks);
     const size_t hi = keep + n * static_cast<size_t>(b + 1) / static_cast<size_t>(a.nblocks);
     const int parity = static_cast<int>(e & 1u);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        a.ll + static_cast<size_t>(a.world * parity + a.rank) * a.ll_stride, 0,
-        static_cast<int>(a.ll_stride * 16), kRawBufferDword3);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    uint64_t *mine = a.ll + static_cast<size_t>(a.world * parity + a.rank) * a.ll_stride;
     for (size_t u = lo + threadIdx.x; u < hi; u += kExchThreads) {
-        __builtin_amdgcn_raw_buffer_store_b128(zero, r, static_cast<int>(u * 16), 0, kSysCoherent);
-        __builtin_amdgcn_raw_buffer_store_b128(zero, r, static_cast<int>((half + u) * 16), 0, kSysCoherent);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            __hip_atomic_store(mine + k * plane + u, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
+    // settle the zeros on this rare path, so that the common path does not
+    // inherit a wait for them (see the low-latency kernel's publish)
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Loads and stores share one counter on this GPU (vmcnt), and the compiler
@@ -608,25 +619,53 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
 // slot stores acknowledged before it raises its flag, and a peer must see
 // the flag before it may read the slot.  Here the data carries its own
 // readiness, in the manner of the low-latency protocol of NCCL and RCCL:
-// every 8-byte word written to host memory holds 4 bytes of values and the
-// call number e, so a reader that finds e in a word also holds that word's
-// values (8-byte aligned stores and loads are single accesses all the way to
-// host memory, so a word is never seen half written).  There is no flag, no
-// acknowledgement wait and no separate read; the price is twice the bytes on
-// the link, which is why only small calls take this path.
+// every 8-byte word written to host memory holds 6 bytes of values and a
+// 16-bit call field, so a reader that finds the call's field in a word also
+// holds that word's values.  Every word is written and read as one naturally
+// aligned 64-bit relaxed system-scope atomic, whose single-copy atomicity is
+// what makes a word never seen half written.  There is no flag, no
+// acknowledgement wait and no separate read; the price is 4/3 of the bytes
+// on the link, which is why only small calls take this path.
 //
-// Layout: LL slot [e & 1][q] holds two halves of ll_stride / 2 16-byte
-// words; for each 8-value unit u of the call, word u of the first half is
-// {v0v1, e, v2v3, e} and word u of the second {v4v5, e, v6v7, e}; the last
-// unit's missing values are zero.  One unit per lane: active workgroup b owns the
+// Layout: LL slot [e & 1][q] holds three planes of ll_stride / 3 words; for
+// each 8-value unit u of the call (x = {v0v1, v2v3, v4v5, v6v7}), word u of
+// plane 0 is v0 v1 v2, of plane 1 v3 v4 v5, of plane 2 v6 v7 and a zero
+// value, each with the call field in its top 16 bits; the last unit's
+// missing values are zero.  Each store and load instruction covers 64
+// consecutive words of one plane (whole lines; an interleaved layout makes
+// partial-line writes to host memory, which the link carries at a small
+// fraction of its rate).  One unit per lane: active workgroup b owns the
 // units [nunits*b/nact, nunits*(b+1)/nact).  Each lane publishes its unit,
-// then polls the two words of that unit in every peer's slot (all peers at
-// once) until every word carries e; after a barrier the workgroup folds left
-// in rank order and stores, or, if any lane of it timed out or saw an abort,
-// stores nothing.  No word of an earlier call carries e's low 32 bits (see
-// ll_clear); parity safety is the one-shot's argument, with "flag" read as
-// "word".
+// then polls the three words of that unit in every peer's slot (all peers at
+// once) until every word carries the call's field; after a barrier the
+// workgroup folds left in rank order and stores, or, if any lane of it timed
+// out or saw an abort, stores nothing.  No word of an earlier call carries
+// the call's field (see ll_clear); parity safety is the one-shot's argument,
+// with "flag" read as "word".
+__device__ __forceinline__ uint64_t ll_field(uint64_t e) {
+    return static_cast<uint64_t>((static_cast<uint32_t>(e) & 0x7FFFu) | 0x8000u) << 48;
+}
+__device__ __forceinline__ uint64_t ll_word0(u32x4 x) { return x.x | (static_cast<uint64_t>(x.y & 0xFFFFu) << 32); }
+__device__ __forceinline__ uint64_t ll_word1(u32x4 x) { return (x.y >> 16) | (static_cast<uint64_t>(x.z) << 16); }
+__device__ __forceinline__ uint64_t ll_word2(u32x4 x) { return x.w; }
+__device__ __forceinline__ u32x4 ll_unpack(uint64_t w0, uint64_t w1, uint64_t w2) {
+    u32x4 x;
+    x.x = static_cast<uint32_t>(w0);
+    x.y = (static_cast<uint32_t>(w0 >> 32) & 0xFFFFu) | (static_cast<uint32_t>(w1) << 16);
+    x.z = static_cast<uint32_t>(w1 >> 16);
+    x.w = static_cast<uint32_t>(w2);
+    return x;
+}
 constexpr size_t kLLMaxNumel = 32768;      // values per call the LL slots hold
+
+// 8-byte words per LL slot of a channel of max_numel values: three planes
+// of one word per 8-value unit, each plane a whole number of 128-byte lines.
+inline size_t ll_stride_for(size_t max_numel) {
+    const size_t ll_max = max_numel < kLLMaxNumel ? max_numel : kLLMaxNumel;
+    const size_t units = (ll_max + kVecElems - 1) / kVecElems;
+    const size_t per_line = kLine / sizeof(uint64_t);
+    return 3 * ((units + per_line - 1) / per_line * per_line);
+}
 // Largest call the automatic choice gives LL: its doubled bytes and its
 // readers polling every peer's data cost more as the group grows.  Measured
 // on MI355X, graph-captured (two ranks on two loopback streams, larger groups
@@ -683,31 +722,36 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
         }
     }
 
-    const uint64_t e64 = next_call(a, b);  // its barrier also orders s_status's reset
+    // the counter's store is deferred to after the polling (see the publish)
+    const uint64_t e64 = next_call(a, b, false);  // its barrier also orders s_status's reset
     if (e64 == 0) return;
     if (ll_clear_due(e64)) ll_clear(a, b, e64, nunits);
-    if (!active) return;
+    if (!active) {
+        commit_call(a, b, e64);
+        return;
+    }
     const uint64_t tl1 = HR_NOW();
-    const uint32_t e = static_cast<uint32_t>(e64);  // the words carry the low 32 bits (never 0)
+    const uint64_t field = ll_field(e64);
     const int parity = static_cast<int>(e64 & 1u);
     const int rank = a.rank;
+    const size_t plane = a.ll_stride / 3;
+    const uint64_t *slot0 = a.ll + static_cast<size_t>(W * parity) * a.ll_stride + u;  // rank 0's word 0 of unit u
 
-    __amdgpu_buffer_rsrc_t ll[W];
-#pragma unroll
-    for (int q = 0; q < W; ++q)
-        ll[q] = __builtin_amdgcn_make_buffer_rsrc(a.ll + static_cast<size_t>(W * parity + q) * a.ll_stride, 0,
-                                                  static_cast<int>(a.ll_stride * 16), kRawBufferDword3);
-    // word 0 of every unit, then word 1 of every unit: each store and load
-    // instruction covers 64 consecutive 16-byte words (whole lines; an
-    // interleaved layout makes partial-line writes to host memory, which the
-    // link carries at a small fraction of its rate)
-    const int off0 = static_cast<int>(u * 16), off1 = static_cast<int>((a.ll_stride / 2 + u) * 16);
-
-    // publish: both words of the unit, system-coherent, no wait
+    // publish: the unit's three words, relaxed 64-bit system-scope stores, no
+    // wait.  On this GPU vmcnt counts stores as well as loads, and the
+    // compiler waits for every outstanding access before it reuses a
+    // register that an outstanding store reads; a reuse between here and the
+    // first poll would make every lane wait for its words' acknowledgement
+    // (a host-link round trip) before polling.  So the store operands stay
+    // live until after the polling (the empty asm below), and the call
+    // counter's own store comes after it too.
+    uint64_t *const m0 = a.ll + static_cast<size_t>(W * parity + rank) * a.ll_stride + u;
+    uint64_t *const m1 = m0 + plane, *const m2 = m0 + 2 * plane;
+    const uint64_t s0 = ll_word0(x) | field, s1 = ll_word1(x) | field, s2 = ll_word2(x) | field;
     if (has) {
-        const u32x4 w0 = {x.x, e, x.y, e}, w1 = {x.z, e, x.w, e};
-        __builtin_amdgcn_raw_buffer_store_b128(w0, ll[rank], off0, 0, kSysCoherent);
-        __builtin_amdgcn_raw_buffer_store_b128(w1, ll[rank], off1, 0, kSysCoherent);
+        __hip_atomic_store(m0, s0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(m1, s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(m2, s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     const uint64_t tl2 = HR_NOW();
 
@@ -715,7 +759,7 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
     // acknowledged (the peers wrote theirs at about the same time)
     if (kLLAckFirst) __builtin_amdgcn_s_waitcnt(0);
 
-    // gather: poll every pending peer's two words until both carry e
+    // gather: poll every pending peer's three words until all carry the field
     u32x4 got[W];
     unsigned pending = has ? (((1u << W) - 1u) & ~(1u << rank)) : 0u;
     uint32_t status = 0;
@@ -724,18 +768,21 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
     for (;;) {
         HR_COUNT(polls);
         // all pending peers' loads in flight at once
-        u32x4 w0[W], w1[W];
+        uint64_t w0[W], w1[W], w2[W];
 #pragma unroll
         for (int q = 0; q < W; ++q) {
             if ((pending >> q) & 1u) {
-                w0[q] = __builtin_amdgcn_raw_buffer_load_b128(ll[q], off0, 0, kSysCoherent);
-                w1[q] = __builtin_amdgcn_raw_buffer_load_b128(ll[q], off1, 0, kSysCoherent);
+                const uint64_t *p = slot0 + static_cast<size_t>(q) * a.ll_stride;
+                w0[q] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                w1[q] = __hip_atomic_load(p + plane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                w2[q] = __hip_atomic_load(p + 2 * plane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             }
         }
 #pragma unroll
         for (int q = 0; q < W; ++q) {
-            if (((pending >> q) & 1u) && w0[q].y == e && w0[q].w == e && w1[q].y == e && w1[q].w == e) {
-                got[q] = u32x4{w0[q].x, w0[q].z, w1[q].x, w1[q].z};
+            if (((pending >> q) & 1u) && ((w0[q] ^ field) >> 48) == 0 && ((w1[q] ^ field) >> 48) == 0 &&
+                ((w2[q] ^ field) >> 48) == 0) {
+                got[q] = ll_unpack(w0[q], w1[q], w2[q]);
                 pending &= ~(1u << q);
             }
         }
@@ -756,8 +803,10 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
         __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.host_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
+    asm volatile("" ::"v"(s0), "v"(s1), "v"(s2), "v"(m0), "v"(m1), "v"(m2));
     const uint64_t tl3 = HR_NOW();
     __syncthreads();
+    commit_call(a, b, e64);
     if (s_status != 0 || !has) return;
     const uint64_t tl4 = HR_NOW();
 
@@ -1181,10 +1230,9 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->flags_off = ch->reduced_off + 2 * ch->stride * sizeof(uint16_t);
     ch->flags2_off = ch->flags_off + flag_bytes;
     ch->ll_off = ch->flags2_off + flag_bytes;
-    // two 16-byte words per 8-value unit of the largest LL call
-    const size_t ll_max = max_numel < kLLMaxNumel ? max_numel : kLLMaxNumel;
-    ch->ll_stride = 2 * ((ll_max + kVecElems - 1) / kVecElems);
-    ch->error_off = ch->ll_off + round_up(2 * static_cast<size_t>(world) * ch->ll_stride * sizeof(u32x4), kLine);
+    // three 8-byte words per 8-value unit of the largest LL call
+    ch->ll_stride = ll_stride_for(max_numel);
+    ch->error_off = ch->ll_off + round_up(2 * static_cast<size_t>(world) * ch->ll_stride * sizeof(uint64_t), kLine);
     ch->abort_off = ch->error_off + kLine;
     ch->host_bytes = ch->abort_off + kLine;
 
@@ -1237,7 +1285,7 @@ ExchArgs call_args(hr_channel ch, int rank, size_t numel, Algo *algo_out) {
     a.flags = reinterpret_cast<uint64_t *>(ch->host_dev + ch->flags_off);
     a.flags2 = reinterpret_cast<uint64_t *>(ch->host_dev + ch->flags2_off);
     a.reduced = reinterpret_cast<uint16_t *>(ch->host_dev + ch->reduced_off);
-    a.ll = reinterpret_cast<u32x4 *>(ch->host_dev + ch->ll_off);
+    a.ll = reinterpret_cast<uint64_t *>(ch->host_dev + ch->ll_off);
     a.ll_stride = ch->ll_stride;
     a.epochs = ch->dev_epochs + static_cast<size_t>(rank) * ch->nblocks;
     a.dev_error = ch->dev_error;
@@ -1474,15 +1522,14 @@ struct NoAllocLayout {
 inline NoAllocLayout noalloc_layout(int world, int nb) {
     NoAllocLayout L{};
     L.stride = round_up(kNoAllocMaxNumel, kLine / sizeof(uint16_t));
-    const size_t ll_max = kNoAllocMaxNumel < kLLMaxNumel ? kNoAllocMaxNumel : kLLMaxNumel;
-    L.ll_stride = 2 * ((ll_max + kVecElems - 1) / kVecElems);
+    L.ll_stride = ll_stride_for(kNoAllocMaxNumel);
     const size_t flag_bytes = static_cast<size_t>(world) * static_cast<size_t>(nb) * kLine;
     L.slots = 0;
     L.reduced = round_up(2 * static_cast<size_t>(world) * L.stride * sizeof(uint16_t), kLine);
     L.flags = L.reduced + round_up(2 * L.stride * sizeof(uint16_t), kLine);
     L.flags2 = L.flags + flag_bytes;
     L.ll = L.flags2 + flag_bytes;
-    L.epochs = L.ll + round_up(2 * static_cast<size_t>(world) * L.ll_stride * sizeof(u32x4), kLine);
+    L.epochs = L.ll + round_up(2 * static_cast<size_t>(world) * L.ll_stride * sizeof(uint64_t), kLine);
     L.dev_error = L.epochs + round_up(static_cast<size_t>(world) * nb * sizeof(uint64_t), kLine);
     L.host_error = L.dev_error + kLine;
     L.abort_w = L.host_error + kLine;
@@ -1593,7 +1640,7 @@ extern "C" HR_API hr_status hr_allreduce_group_noalloc_f16(const void *const *in
     a.flags = reinterpret_cast<uint64_t *>(base + L.flags);
     a.flags2 = reinterpret_cast<uint64_t *>(base + L.flags2);
     a.reduced = reinterpret_cast<uint16_t *>(base + L.reduced);
-    a.ll = reinterpret_cast<u32x4 *>(base + L.ll);
+    a.ll = reinterpret_cast<uint64_t *>(base + L.ll);
     a.ll_stride = L.ll_stride;
     a.epochs = reinterpret_cast<uint64_t *>(base + L.epochs);
     a.dev_error = reinterpret_cast<uint32_t *>(base + L.dev_error);
@@ -1622,8 +1669,9 @@ extern "C" HR_API hr_status hr_allreduce_group_noalloc_f16(const void *const *in
     c.base[1] = reinterpret_cast<u32x4 *>(base + L.epochs);
     c.units[1] = static_cast<uint32_t>((L.total - L.epochs) / sizeof(u32x4));
     if (algo == Algo::ll) {
-        c.base[2] = reinterpret_cast<u32x4 *>(base + L.ll) + static_cast<size_t>(W) * L.ll_stride;
-        c.units[2] = static_cast<uint32_t>(static_cast<size_t>(W) * L.ll_stride);
+        // parity 1's slots: W x ll_stride 8-byte words, a whole number of 16-byte units
+        c.base[2] = reinterpret_cast<u32x4 *>(base + L.ll + static_cast<size_t>(W) * L.ll_stride * sizeof(uint64_t));
+        c.units[2] = static_cast<uint32_t>(static_cast<size_t>(W) * L.ll_stride * sizeof(uint64_t) / sizeof(u32x4));
     }
     c.word = status;
     const uint32_t units = c.units[0] > c.units[2] ? c.units[0] : c.units[2];

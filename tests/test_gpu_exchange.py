@@ -279,21 +279,28 @@ def test_host_acts_as_the_peer(streams):
         ch.destroy()
 
 
-def ll_words(bits, call, half_words):
-    """The low-latency slot image of one contribution: two halves of
-    half_words 16-byte words; unit u (8 values, the last one zero-padded) is
-    word u of the first half, {v0v1, call, v2v3, call}, and word u of the
-    second, {v4v5, call, v6v7, call}."""
+def ll_field(call):
+    """The 16-bit call field of a low-latency word (hr.h): the call number's
+    low 15 bits with the top bit set."""
+    return (call & 0x7FFF) | 0x8000
+
+
+def ll_words(bits, call, plane_words):
+    """The low-latency slot image of one contribution (hr.h): three planes of
+    plane_words 64-bit words; unit u (values v0..v7, the last unit
+    zero-padded) is word u of each plane -- v0 v1 v2, v3 v4 v5 and v6 v7 0 in
+    bits 0..47 -- with the call field in bits 48..63."""
     n = bits.size
     units = -(-n // 8)
-    v = np.zeros(units * 8, np.uint16)
+    v = np.zeros(units * 8, np.uint64)
     v[:n] = bits
-    pairs = v.view(np.uint32).reshape(units, 4)
-    img = np.zeros((2, half_words, 4), np.uint32)
-    img[0, :units, 0], img[0, :units, 2] = pairs[:, 0], pairs[:, 1]
-    img[1, :units, 0], img[1, :units, 2] = pairs[:, 2], pairs[:, 3]
-    img[:, :units, 1] = call
-    img[:, :units, 3] = call
+    v = v.reshape(units, 8)
+    sh = lambda x, k: x << np.uint64(k)
+    f = sh(np.uint64(ll_field(call)), 48)
+    img = np.zeros((3, plane_words), np.uint64)
+    img[0, :units] = v[:, 0] | sh(v[:, 1], 16) | sh(v[:, 2], 32) | f
+    img[1, :units] = v[:, 3] | sh(v[:, 4], 16) | sh(v[:, 5], 32) | f
+    img[2, :units] = v[:, 6] | sh(v[:, 7], 16) | f
     return img, units
 
 
@@ -310,18 +317,18 @@ def test_host_acts_as_the_peer_ll(streams, n):
         x0b, x1b = specials_mix(n, 45), specials_mix(n, 46)
         x0 = to_dev(x0b)
         out0 = torch.empty_like(x0)
-        slot_bytes = info.ll_stride * 16
-        half = info.ll_stride // 2
-        peer, _ = ll_words(x1b, 1, half)
+        slot_bytes = info.ll_stride * 8
+        plane = info.ll_stride // 3
+        peer, _ = ll_words(x1b, 1, plane)
         ctypes.memmove(info.host_ll + (2 * 1 + 1) * slot_bytes, peer.ctypes.data, peer.nbytes)
         torch.cuda.synchronize()
         ch.allreduce(0, x0, out0, streams[0])          # call 1 -> parity 1
         streams[0].synchronize()
         assert ch.status() == hr.HR_OK
         assert_same_bits(to_host(out0), oracle.add(x0b, x1b), "host peer, LL")
-        own, units = ll_words(x0b, 1, half)
+        own, units = ll_words(x0b, 1, plane)
         seen = np.frombuffer(ctypes.string_at(info.host_ll + (2 * 1 + 0) * slot_bytes, slot_bytes),
-                             dtype=np.uint32).reshape(2, half, 4)
+                             dtype=np.uint64).reshape(3, plane)
         assert np.array_equal(seen[:, :units], own[:, :units])
     finally:
         torch.cuda.synchronize()
@@ -609,8 +616,8 @@ def _peer_flags(info, value):
 
 
 def _peer_ll_words(info, bits, call, tag):
-    slot_bytes = info.ll_stride * 16
-    img, _ = ll_words(bits, tag, info.ll_stride // 2)
+    slot_bytes = info.ll_stride * 8
+    img, _ = ll_words(bits, tag, info.ll_stride // 3)
     ctypes.memmove(info.host_ll + (2 * (call & 1) + 1) * slot_bytes, img.ctypes.data, img.nbytes)
 
 
@@ -665,40 +672,41 @@ def test_stale_peer_values_do_not_release(streams, algorithm, stale):
 
 
 def _ll_slot(info, parity, rank):
-    slot_bytes = info.ll_stride * 16
+    slot_bytes = info.ll_stride * 8
     raw = ctypes.string_at(info.host_ll + (info.world_size * parity + rank) * slot_bytes, slot_bytes)
-    return np.frombuffer(raw, dtype=np.uint32).reshape(2, info.ll_stride // 2, 4).copy()
+    return np.frombuffer(raw, dtype=np.uint64).reshape(3, info.ll_stride // 3).copy()
+
+
+def _fields(words):
+    return (words >> np.uint64(48)).astype(np.int64)
 
 
 def _plant_ll(info, parity, rank, tag):
-    """Every word of slot[parity][rank] set to {0x3c003c00, tag, 0x3c003c00, tag}:
-    values 1.0, call field `tag`, as a call of that number would leave them."""
-    half = info.ll_stride // 2
-    img = np.zeros((2, half, 4), np.uint32)
-    img[:, :, 0] = img[:, :, 2] = 0x3C003C00
-    img[:, :, 1] = img[:, :, 3] = tag & 0xFFFFFFFF
-    slot_bytes = info.ll_stride * 16
+    """Every word of slot[parity][rank] set to three values 1.0 (0x3c00) and
+    the call field of call `tag`, as a call of that number would leave them."""
+    img = np.full((3, info.ll_stride // 3),
+                  0x3C00 | 0x3C00 << 16 | 0x3C00 << 32 | ll_field(tag) << 48, np.uint64)
+    slot_bytes = info.ll_stride * 8
     ctypes.memmove(info.host_ll + (info.world_size * parity + rank) * slot_bytes, img.ctypes.data,
                    img.nbytes)
 
 
 @pytest.mark.parametrize("first", [hr.HR_ALGO_LL, hr.HR_ALGO_ONE_SHOT], ids=["ll", "one-shot"])
 def test_ll_clearing_removes_words_of_calls_2_32_earlier(streams, first):
-    """Low-latency words carry the low 32 bits of the call number.  Words
-    planted in both ranks' even-parity slots with the low 32 bits of call
-    c + 2 stand for words left by call c + 2 - 2^32 that no later call
-    overwrote.  Call c = 2^31 + 2 is a clearing point of the even parity: both
-    ranks zero their slot there except the units the call itself writes.  So
-    afterwards rank 0 alone at call c + 2 finds nothing to take and ends at
-    its watchdog with `out` unwritten.  At a call that is not a clearing
-    point (c + 4) the planted words stay, which shows the planting is what
-    a reader would see."""
+    """Low-latency words carry a 15-bit call field.  Words planted in both
+    ranks' even-parity slots with the field of call c + 2 stand for words
+    left by call c + 2 - 2^15 that no later call overwrote.  Call
+    c = 2^31 + 2 is a clearing point of the even parity (its low 14 bits are
+    2): both ranks zero their slot there except the units the call itself
+    writes.  So afterwards rank 0 alone at call c + 2 finds nothing to take
+    and ends at its watchdog with `out` unwritten.  At a call that is not a
+    clearing point (c + 2) the planted words stay, which shows the planting
+    is what a reader would see."""
     c = (1 << 31) + 2
     ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=first)
     small = 8                                   # one 8-value unit
     try:
         info = ch.info()
-        half = info.ll_stride // 2
         _counters(ch, c - 1)
         for r in range(2):
             _plant_ll(info, 0, r, c + 2)
@@ -715,7 +723,7 @@ def test_ll_clearing_removes_words_of_calls_2_32_earlier(streams, first):
             slot = _ll_slot(info, 0, r)
             assert not slot[:, keep:].any(), f"rank {r}: planted words survived the clearing call"
             if keep:
-                assert (slot[:, 0, 1] == c).all() and (slot[:, 0, 3] == c).all()
+                assert (_fields(slot[:, 0]) == ll_field(c)).all()
     finally:
         torch.cuda.synchronize()
         ch.destroy()
@@ -758,8 +766,8 @@ def test_ll_clearing_removes_words_of_calls_2_32_earlier(streams, first):
         check_pair(out0, out1, x0b, x1b, f"call {c + 2}")
         for r in range(2):
             slot = _ll_slot(info, 0, r)
-            assert (slot[:, 1:, 1] == ((c + 4) & 0xFFFFFFFF)).all()
-            assert (slot[:, 0, 1] == c + 2).all()
+            assert (_fields(slot[:, 1:]) == ll_field(c + 4)).all()
+            assert (_fields(slot[:, 0]) == ll_field(c + 2)).all()
     finally:
         torch.cuda.synchronize()
         ch.destroy()
