@@ -666,19 +666,22 @@ inline size_t ll_stride_for(size_t max_numel) {
     const size_t per_line = kLine / sizeof(uint64_t);
     return 3 * ((units + per_line - 1) / per_line * per_line);
 }
-// Largest call the automatic choice gives LL: its doubled bytes and its
+// Largest call the automatic choice gives LL: its extra bytes (4/3) and its
 // readers polling every peer's data cost more as the group grows.  Measured
 // on MI355X, graph-captured (two ranks on two loopback streams, larger groups
-// in one group launch), as the largest size at which LL beat the one-shot:
-// W = 2 12288, W = 3 6144, W = 4 3072, W = 5 and 6 1024, W = 7 and 8 512.
+// in one group launch), as the largest size at which LL beat the one-shot on
+// two boxes: W = 2 16384, W = 3 6144, W = 4 4096, W = 5 to 7 2048, W = 8
+// 1024 (e.g. W = 2 at 16384 values 6.5 against 7.1-7.4 us, W = 8 at 1024
+// 7.5-7.8 against 8.2-8.7 us).
 inline size_t ll_auto_max_numel(int world) {
     switch (world) {
-        case 2: return 12288;
+        case 2: return 16384;
         case 3: return 6144;
-        case 4: return 3072;
+        case 4: return 4096;
         case 5:
-        case 6: return 1024;
-        default: return 512;
+        case 6:
+        case 7: return 2048;
+        default: return 1024;
     }
 }
 // A lane polls as soon as its own words are issued and sleeps only briefly
@@ -951,16 +954,18 @@ inline int active_blocks(size_t numel, int nblocks, int world) {
 // automatic choice: the one-shot reads W - 1 peers' whole contributions, the
 // two-shot 2 (W - 1) / W of one, but its second handshake adds latency, so
 // the crossover falls as the group grows.  Measured on MI355X with every rank
-// in one group launch (graph-captured), as the first of 512 .. 131072 values
-// at which the two-shot was faster: W = 3 98304, W = 4 and 5 16384, W = 6
-// 8192, W = 7 and 8 4096.
+// in one group launch (graph-captured), as the first size at which the
+// two-shot was faster in two rounds: W = 3 98304, W = 4 16384, W = 5 10240,
+// W = 6 6144, W = 7 4096, W = 8 3072 (e.g. W = 5 at 10240 values 13.6-13.8
+// against 14.2 us, W = 8 at 3072 12.0-12.6 against 12.7-13.1 us).
 inline size_t two_shot_min_numel(int world) {
     switch (world) {
         case 3: return 98304;
-        case 4:
-        case 5: return 16384;
-        case 6: return 8192;
-        default: return 4096;
+        case 4: return 16384;
+        case 5: return 10240;
+        case 6: return 6144;
+        case 7: return 4096;
+        default: return 3072;
     }
 }
 

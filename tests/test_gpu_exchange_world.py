@@ -172,7 +172,7 @@ def test_missing_rank_times_out_every_waiting_rank(algo):
 
 
 def test_automatic_choice_mixes_algorithms_across_calls():
-    """Under HR_ALGO_AUTO a W = 4 channel takes LL up to 3072 values, the
+    """Under HR_ALGO_AUTO a W = 4 channel takes LL up to 4096 values, the
     one-shot below 16384 and the two-shot from there; alternating sizes
     alternate the algorithm while the slot parity keeps advancing."""
     W = 4
