@@ -89,6 +89,7 @@ constexpr int kExchUnroll = 4;                    // units per lane per publish 
 constexpr int kMaxWorld = 8;
 constexpr int kMinActivePolls = 16;                // W * minimum active workgroups
 constexpr uint32_t kAbortAfterUs = 20;             // waits read the abort word only after this long
+constexpr uint32_t kLLLeadNs = 400;                // an LL poll's lead over the words it should find
 constexpr size_t kLine = 128;                     // bytes per flag / word line
 constexpr size_t kFlagStride = kLine / sizeof(uint64_t);  // flags are 64-bit call numbers
 
@@ -109,6 +110,7 @@ struct ExchArgs {
     const uint32_t *abort_w;  // device view of the host abort word
     uint64_t timeout_ticks;
     uint64_t abort_after_ticks;  // waits shorter than this do not read the abort word
+    uint32_t ll_lead_ticks;   // LL: a read's lead over the last word it should find
     uint32_t pace_q16;        // wall-clock ticks per byte of a paced publish, x 2^16 (0: unpaced)
     int rank;
     int world;
@@ -762,6 +764,21 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
     // acknowledged (the peers wrote theirs at about the same time)
     if (kLLAckFirst) __builtin_amdgcn_s_waitcnt(0);
 
+    // hold the first poll until the call's words have nearly drained from
+    // the host link: a read does not pass the writes issued before it, and
+    // one that reaches host memory before the peer's words costs a second
+    // round trip.  The link carries all W ranks' words (24 bytes per unit)
+    // at the channel's pacing rate; the poll leaves ll_lead_ticks early, the
+    // time its request takes to reach host memory
+    if (has && a.pace_q16 != 0) {
+        const uint64_t drain = (static_cast<uint64_t>(W) * nunits * 24u * a.pace_q16) >> 16;
+        if (drain > a.ll_lead_ticks) {
+            const uint64_t hold = drain - a.ll_lead_ticks;
+            const long long tw = wall_clock64();
+            while (static_cast<uint64_t>(wall_clock64() - tw) < hold) __builtin_amdgcn_s_sleep(1);
+        }
+    }
+
     // gather: poll every pending peer's three words until all carry the field
     u32x4 got[W];
     unsigned pending = has ? (((1u << W) - 1u) & ~(1u << rank)) : 0u;
@@ -1077,6 +1094,7 @@ struct hr_channel_s {
     uint32_t timeout_us;
     uint64_t timeout_ticks;
     uint64_t abort_after_ticks;
+    uint32_t ll_lead_ticks;
     uint32_t link_mbps;        // pacing rate, or HR_LINK_UNPACED
     uint32_t pace_q16;         // wall-clock ticks per byte x 2^16, 0 when unpaced
     void *host_base;           // hipHostMalloc'ed region (host address)
@@ -1227,6 +1245,7 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->timeout_us = timeout_us;
     ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
     ch->abort_after_ticks = static_cast<uint64_t>(kAbortAfterUs) * static_cast<uint64_t>(clock_khz) / 1000u;
+    ch->ll_lead_ticks = static_cast<uint32_t>(static_cast<uint64_t>(kLLLeadNs) * static_cast<uint64_t>(clock_khz) / 1000000u);
     ch->link_mbps = cfg->link_mbps;  // 0: the device's measured rate, below
 
     const size_t slot_bytes = 2 * static_cast<size_t>(world) * ch->stride * sizeof(uint16_t);
@@ -1298,6 +1317,7 @@ ExchArgs call_args(hr_channel ch, int rank, size_t numel, Algo *algo_out) {
     a.abort_w = reinterpret_cast<const uint32_t *>(ch->host_dev + ch->abort_off);
     a.timeout_ticks = ch->timeout_ticks;
     a.abort_after_ticks = ch->abort_after_ticks;
+    a.ll_lead_ticks = ch->ll_lead_ticks;
     a.pace_q16 = ch->pace_q16;
     a.rank = rank;
     a.world = ch->world_size;
