@@ -13,8 +13,9 @@ workgroup), counter (loading the first input batch and advancing the call
 counter), pace (its turn on the host link), publish (slot stores, their
 acknowledgement, the flag), wait (the peers' flags), combine (peer reads,
 fold, stores).  Of a low-latency (LL) workgroup: entry, counter, publish
-(issuing the words), lane 0's polling until its peer words carry the call
-number, the rest of the workgroup (the barrier), and the fold and stores.
+(issuing the words), lane 0's hold before its first poll and its polling
+until its peer words carry the call's field, the rest of the workgroup (the
+barrier), and the fold and stores.
 "gap" is the time from a call's last workgroup ending to the next call's
 first workgroup starting (the kernel's end and the next graph node's
 dispatch).  The clock's rate is taken from the same replay: stamp ticks over
@@ -139,7 +140,7 @@ def analyse(rec, elapsed, algo):
           "counter": tc[:, 1] - tc[:, 0]}
     if algo == hr.HR_ALGO_LL:
         ph.update({"publish (issue words)": tc[:, 2] - tc[:, 1],
-                   "lane 0 polls until its peer words match": tc[:, 3] - tc[:, 2],
+                   "lane 0's hold and polls until its peer words match": tc[:, 3] - tc[:, 2],
                    "rest of the workgroup (barrier)": tc[:, 4] - tc[:, 3],
                    "fold + store": tc[:, 5] - tc[:, 4]})
     else:
