@@ -120,7 +120,7 @@ typedef enum {
 #define HR_ALGO_LL 3        /* low-latency one-shot: every 8-byte word in
                                host memory carries 6 bytes of values and a
                                16-bit call field, so readers poll the data
-                               itself (no flags); 4/3 of the link bytes; up
+                               itself (no flags); 3/2 of the link bytes; up
                                to 32768 values (larger calls: one-shot)   */
 
 typedef struct {

@@ -626,8 +626,9 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
 // holds that word's values.  Every word is written and read as one naturally
 // aligned 64-bit relaxed system-scope atomic, whose single-copy atomicity is
 // what makes a word never seen half written.  There is no flag, no
-// acknowledgement wait and no separate read; the price is 4/3 of the bytes
-// on the link, which is why only small calls take this path.
+// acknowledgement wait and no separate read; the price is 3/2 of the bytes
+// on the link (three words for a unit of 8 values, the last word holding
+// two), which is why only small calls take this path.
 //
 // Layout: LL slot [e & 1][q] holds three planes of ll_stride / 3 words; for
 // each 8-value unit u of the call (x = {v0v1, v2v3, v4v5, v6v7}), word u of
@@ -668,7 +669,7 @@ inline size_t ll_stride_for(size_t max_numel) {
     const size_t per_line = kLine / sizeof(uint64_t);
     return 3 * ((units + per_line - 1) / per_line * per_line);
 }
-// Largest call the automatic choice gives LL: its extra bytes (4/3) and its
+// Largest call the automatic choice gives LL: its extra bytes (3/2) and its
 // readers polling every peer's data cost more as the group grows.  Measured
 // on MI355X, graph-captured (two ranks on two loopback streams, larger groups
 // in one group launch), as the largest size at which LL beat the one-shot on
