@@ -76,6 +76,9 @@ def parse():
                    default=None,
                    help="run one kernel --reps times and nothing else (for rocprofv3 counters)")
     p.add_argument("--reps", type=int, default=10)
+    p.add_argument("--numel", type=int, default=0,
+                   help="values per rank of the exchange profiling target (0: workload 2 at "
+                        "32 tokens, 131072); smaller sizes take the first values of it")
     p.add_argument("--num-blocks", type=int, default=0,
                    help="workgroups per rank of the channel the exchange profiling target makes "
                         "(0: the library's default)")
@@ -785,7 +788,7 @@ def measured_traffic(kernel):
 
 # ------------------------------------------------------- profiling targets
 
-def profile_kernel(which, reps, link_mbps=0, num_blocks=0):
+def profile_kernel(which, reps, link_mbps=0, num_blocks=0, numel=0):
     """Launch one kernel `reps` times with nothing else timed, for
     rocprofv3 (counter collection serialises dispatches, so the exchange runs
     one rank against a peer that the host plays: the host writes the peer's
@@ -845,11 +848,17 @@ def profile_kernel(which, reps, link_mbps=0, num_blocks=0):
             f"{'workspaces' if which == 'fold' else 'sets of separate tensors'}, bit_exact={ok}")
         return
     x0b, x1b = inputs.workload2(32)
+    if numel:
+        if not 0 < numel <= x0b.size:
+            raise ValueError(f"--numel must be in 1..{x0b.size}")
+        x0b, x1b = x0b[:numel].copy(), x1b[:numel].copy()
     n = x0b.size
     x0 = to_dev(x0b)
     out = torch.empty_like(x0)
     streams = hr.LoopbackStreams(0)
-    ch = hr.Channel(timeout_us=2_000_000, link_mbps=link_mbps, num_blocks=num_blocks)
+    # the one-shot at every size: the host-played peer follows its protocol
+    ch = hr.Channel(timeout_us=2_000_000, link_mbps=link_mbps, num_blocks=num_blocks,
+                    algorithm=hr.HR_ALGO_ONE_SHOT)
     info = ch.info()
     algo = ch.algorithm_for(n)
     if algo != hr.HR_ALGO_ONE_SHOT:
@@ -886,7 +895,7 @@ def main():
               f"(--gpus {args.gpus} requested); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.profile_kernel:
-        profile_kernel(args.profile_kernel, args.reps, args.link_mbps, args.num_blocks)
+        profile_kernel(args.profile_kernel, args.reps, args.link_mbps, args.num_blocks, args.numel)
         return
     c = Ctx()
     torch = c.torch
