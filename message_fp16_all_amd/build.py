@@ -28,6 +28,9 @@ FLAGS = [
     "-fvisibility=hidden",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernels receive their first five arguments in SGPRs (the per-rank
+    # exchange kernels put what their first loads need there)
+    "-mllvm", "-amdgpu-kernarg-preload-count=5",
     "-I", INCLUDE,
     "-Wl,-rpath,/opt/rocm/lib",
 ]
