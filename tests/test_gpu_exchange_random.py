@@ -134,3 +134,46 @@ def test_low_latency_graph_replayed_with_fresh_inputs():
         torch.cuda.synchronize()
         ch.destroy()
         streams.destroy()
+
+
+@pytest.mark.parametrize("world,launch", [(2, "per-rank"), (4, "per-rank"), (4, "group"), (8, "group")],
+                         ids=["W2-per-rank", "W4-per-rank", "W4-group", "W8-group"])
+def test_random_sizes_queued_without_host_sync(world, launch):
+    """A seeded sequence of calls whose sizes cross every switch point of the
+    automatic choice (so consecutive calls change algorithm, and with it the
+    slots, flags and low-latency words they use), all queued before the host
+    waits once: ranks run up to a call apart on the device, which is when the
+    double buffering by call parity (the 1Cat-vLLM page, "Purpose") has to
+    hold.  Each call has its own buffers; every output is then compared with
+    the oracle's left fold."""
+    calls, max_numel = 240, 1 << 18
+    rng = np.random.default_rng(4100 + world + (100 if launch == "group" else 0))
+    streams = hr.LoopbackStreams(0, n=world) if launch == "per-rank" else None
+    group_stream = torch.cuda.Stream() if launch == "group" else None
+    ch = hr.Channel(world_size=world, max_numel=max_numel, timeout_us=2_000_000)
+    try:
+        sizes = [int(min(max_numel, max(1, round(2 ** rng.uniform(0, 18))))) for _ in range(calls)]
+        algos = {ch.algorithm_for(n) for n in sizes}
+        assert algos == {hr.HR_ALGO_LL, hr.HR_ALGO_ONE_SHOT} | ({hr.HR_ALGO_TWO_SHOT} if world > 2 else set())
+        xb = [[specials_mix(n, seed=int(rng.integers(0, 1 << 30))) for _ in range(world)] for n in sizes]
+        xs = [[to_dev(b) for b in row] for row in xb]
+        outs = [[torch.empty_like(x) for x in row] for row in xs]
+        torch.cuda.synchronize()
+        print(f"queueing {calls} calls, W={world} {launch}, algorithms {sorted(algos)}", flush=True)
+        for c in range(calls):
+            if launch == "group":
+                ch.allreduce_group(xs[c], outs[c], group_stream)
+            else:
+                for r in rng.permutation(world):
+                    ch.allreduce(int(r), xs[c][int(r)], outs[c][int(r)], streams[int(r)])
+        torch.cuda.synchronize()
+        assert ch.status() == hr.HR_OK, hr.hr_status_str(ch.status())
+        for c in range(calls):
+            ref = oracle.fold(xb[c])
+            for r in range(world):
+                assert_same_bits(to_host(outs[c][r]), ref, f"call {c} n={sizes[c]} rank {r}")
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+        if streams is not None:
+            streams.destroy()
