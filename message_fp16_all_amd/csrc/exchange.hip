@@ -687,14 +687,13 @@ inline size_t ll_auto_max_numel(int world) {
         default: return 1024;
     }
 }
-// A lane polls as soon as its own words are issued and sleeps only briefly
-// between polls.  Measured on MI355X, two ranks in loopback, graph-captured,
-// against waiting for the own stores' acknowledgement before the first poll
-// and sleeping 8 x 64 clocks: 4096 values 4.98-5.41 -> 4.86-4.91 us, 12288
+// A lane does not wait for its own words' acknowledgement before polling,
+// and it sleeps only briefly between polls.  Measured on MI355X, two ranks
+// in loopback, graph-captured, against waiting for the acknowledgement and
+// sleeping 8 x 64 clocks: 4096 values 4.98-5.41 -> 4.86-4.91 us, 12288
 // values 6.59-7.02 -> 6.20-6.27 us.  The polls read host memory, so a lane
 // has at most one in flight and the round trip, not the sleep, sets the
 // polling rate.
-constexpr bool kLLAckFirst = false;        // first poll after the own words are acknowledged
 constexpr int kLLSleep = 1;                // s_sleep after a failed poll (x 64 clocks)
 
 template <int W, bool VEC, class E>
@@ -760,10 +759,6 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
         __hip_atomic_store(m2, s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     const uint64_t tl2 = HR_NOW();
-
-    // optionally hold the first poll until this lane's own words are
-    // acknowledged (the peers wrote theirs at about the same time)
-    if (kLLAckFirst) __builtin_amdgcn_s_waitcnt(0);
 
     // hold the first poll until the call's words have nearly drained from
     // the host link: a read does not pass the writes issued before it, and
