@@ -52,7 +52,11 @@ def say(msg):
     sys.stdout.flush()
 
 
-@pytest.fixture(scope="module", params=[2, 3, 4, 5, 6, 7, 8], ids=lambda w: f"W{w}")
+# every group size with each of its switch points and one value either side
+CASES = [(W, n) for W in range(2, 9) for n in sizes(W)]
+
+
+@pytest.fixture(scope="module")
 def group(request):
     W = request.param
     streams = hr.LoopbackStreams(0, n=W)
@@ -65,13 +69,10 @@ def group(request):
 
 @pytest.mark.parametrize("launch", ["per-rank", "group"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("k", range(6))
-def test_switch_point(group, k, dtype, launch):
+@pytest.mark.parametrize("group,n", CASES, indirect=["group"], ids=[f"W{W}-n{n}" for W, n in CASES])
+def test_switch_point(group, n, dtype, launch):
     W, ch, streams = group
-    ns = sizes(W)
-    if k >= len(ns):
-        pytest.skip("two ranks have no two-shot switch point")
-    n = ns[k]
+    k = sizes(W).index(n)
     want = expected_algorithm(W, n)
     assert ch.algorithm_for(n) == want, f"W={W} n={n}: algorithm {ch.algorithm_for(n)}, table says {want}"
     bf = dtype == "bf16"
