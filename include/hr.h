@@ -107,8 +107,8 @@ typedef enum {
 
 /* Exchange algorithm of a channel (all produce the same bits). */
 #define HR_ALGO_AUTO 0      /* low-latency up to a size that falls with
-                               the group (16384 values at 2 ranks, 6144
-                               at 3, 4096 at 4, 2048 at 5-7, 1024 at 8);
+                               the group (20480 values at 2 ranks, 8192
+                               at 3, 4096 at 4, 2048 at 5-7, 1536 at 8);
                                above it the one-shot, and for 3+ ranks
                                the two-shot from a size that also falls
                                with the group (98304 values at 3 ranks,
@@ -236,7 +236,7 @@ HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out
  * shard in rank order and publish it, and every rank gather the others'
  * folded shards: less host-link traffic for W > 2, the same bits.  The
  * low-latency one-shot (HR_ALGO_LL, or automatic for small calls: up to
- * 16384 values for two ranks, fewer for larger groups) puts a call field
+ * 20480 values for two ranks, fewer for larger groups) puts a call field
  * into every 8-byte word it writes to host memory, so a peer polls the
  * values themselves: no flag, no wait for acknowledgements, one host-link
  * round trip less; the same bits again.

@@ -673,18 +673,20 @@ inline size_t ll_stride_for(size_t max_numel) {
 // readers polling every peer's data cost more as the group grows.  Measured
 // on MI355X, graph-captured (two ranks on two loopback streams, larger groups
 // in one group launch), as the largest size at which LL beat the one-shot on
-// two boxes: W = 2 16384, W = 3 6144, W = 4 4096, W = 5 to 7 2048, W = 8
-// 1024 (e.g. W = 2 at 16384 values 6.5 against 7.1-7.4 us, W = 8 at 1024
-// 7.5-7.8 against 8.2-8.7 us).
+// two boxes: W = 2 20480, W = 3 8192, W = 4 4096, W = 5 to 7 2048, W = 8
+// 1536 (e.g. W = 2 at 20480 values 7.1-7.3 against 7.4-7.5 us and at 24576
+// 8.1-8.2 against 7.6-7.7; W = 3 at 8192 7.6 against 8.2 and at 10240 8.5
+// against 8.3; W = 8 at 1536 9.3 against 9.6-9.8 and at 2048 11.1-11.2
+// against 10.6-10.7).
 inline size_t ll_auto_max_numel(int world) {
     switch (world) {
-        case 2: return 16384;
-        case 3: return 6144;
+        case 2: return 20480;
+        case 3: return 8192;
         case 4: return 4096;
         case 5:
         case 6:
         case 7: return 2048;
-        default: return 1024;
+        default: return 1536;
     }
 }
 // A lane does not wait for its own words' acknowledgement before polling,

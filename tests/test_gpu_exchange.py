@@ -36,7 +36,7 @@ def streams():
     ls.destroy()
 
 
-# AUTO takes the low-latency one-shot up to 16384 values and the one-shot
+# AUTO takes the low-latency one-shot up to 20480 values and the one-shot
 # above; the two-shot is also correct for two ranks (each rank owns half of
 # the values), so the whole two-rank battery runs on every algorithm
 ALGOS = [hr.HR_ALGO_AUTO, hr.HR_ALGO_ONE_SHOT, hr.HR_ALGO_TWO_SHOT, hr.HR_ALGO_LL]
@@ -428,8 +428,8 @@ def test_algorithm_choice():
     chs = (ch2, ch2t, ch2l, ch4, ch4o)
     try:
         assert ch2.algorithm_for(1) == hr.HR_ALGO_LL
-        assert ch2.algorithm_for(16_384) == hr.HR_ALGO_LL
-        assert ch2.algorithm_for(16_385) == hr.HR_ALGO_ONE_SHOT
+        assert ch2.algorithm_for(20_480) == hr.HR_ALGO_LL
+        assert ch2.algorithm_for(20_481) == hr.HR_ALGO_ONE_SHOT
         assert ch2.algorithm_for(131_072) == hr.HR_ALGO_ONE_SHOT
         assert ch2t.algorithm_for(1) == hr.HR_ALGO_TWO_SHOT
         assert ch2l.algorithm_for(32_768) == hr.HR_ALGO_LL
@@ -439,8 +439,8 @@ def test_algorithm_choice():
         assert ch4.algorithm_for(16_384) == hr.HR_ALGO_TWO_SHOT
         assert ch4.algorithm_for(4096) == hr.HR_ALGO_LL
         assert ch4.algorithm_for(4097) == hr.HR_ALGO_ONE_SHOT
-        for W, ll_max, first in ((3, 6144, 98_304), (5, 2048, 10_240), (6, 2048, 6144), (7, 2048, 4096),
-                                 (8, 1024, 3072)):
+        for W, ll_max, first in ((3, 8192, 98_304), (5, 2048, 10_240), (6, 2048, 6144), (7, 2048, 4096),
+                                 (8, 1536, 3072)):
             chw = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
             try:
                 assert chw.algorithm_for(1) == hr.HR_ALGO_LL, W
