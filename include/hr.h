@@ -108,12 +108,12 @@ typedef enum {
 /* Exchange algorithm of a channel (all produce the same bits). */
 #define HR_ALGO_AUTO 0      /* low-latency up to a size that falls with
                                the group (20480 values at 2 ranks, 8192
-                               at 3, 4096 at 4, 2048 at 5-7, 1536 at 8);
-                               above it the one-shot, and for 3+ ranks
-                               the two-shot from a size that also falls
-                               with the group (98304 values at 3 ranks,
-                               16384 at 4, 10240 at 5, 6144 at 6, 4096
-                               at 7, 3072 at 8)                           */
+                               at 3, 4096 at 4 and 5, 2560 at 6, 2048 at
+                               7, 1536 at 8); above it the one-shot, and
+                               for 3+ ranks the two-shot from a size that
+                               also falls with the group (98304 values at
+                               3 ranks, 16384 at 4, 10240 at 5, 6144 at
+                               6, 5120 at 7, 3072 at 8)                   */
 #define HR_ALGO_ONE_SHOT 1  /* every rank reads every peer's contribution */
 #define HR_ALGO_TWO_SHOT 2  /* shard owners fold, then everyone gathers;
                                needs num_blocks >= world_size             */

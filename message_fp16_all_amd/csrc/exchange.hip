@@ -673,18 +673,19 @@ inline size_t ll_stride_for(size_t max_numel) {
 // readers polling every peer's data cost more as the group grows.  Measured
 // on MI355X, graph-captured (two ranks on two loopback streams, larger groups
 // in one group launch), as the largest size at which LL beat the one-shot on
-// two boxes: W = 2 20480, W = 3 8192, W = 4 4096, W = 5 to 7 2048, W = 8
-// 1536 (e.g. W = 2 at 20480 values 7.1-7.3 against 7.4-7.5 us and at 24576
-// 8.1-8.2 against 7.6-7.7; W = 3 at 8192 7.6 against 8.2 and at 10240 8.5
-// against 8.3; W = 8 at 1536 9.3 against 9.6-9.8 and at 2048 11.1-11.2
-// against 10.6-10.7).
+// two boxes: W = 2 20480, W = 3 8192, W = 4 4096, W = 5 4096, W = 6 2560,
+// W = 7 2048, W = 8 1536 (e.g. W = 2 at 20480 values 7.1-7.3 against
+// 7.4-7.5 us and at 24576 8.1-8.2 against 7.6-7.7; W = 3 at 8192 7.6 against
+// 8.2 and at 10240 8.5 against 8.3; W = 5 at 4096 9.5 against 9.6; W = 6 at
+// 2560 8.9 against 8.9-9.0 and at 3072 9.8 against 9.4-9.5; W = 8 at 1536
+// 9.3 against 9.6-9.8 and at 2048 11.1-11.2 against 10.6-10.7).
 inline size_t ll_auto_max_numel(int world) {
     switch (world) {
         case 2: return 20480;
         case 3: return 8192;
         case 4: return 4096;
-        case 5:
-        case 6:
+        case 5: return 4096;
+        case 6: return 2560;
         case 7: return 2048;
         default: return 1536;
     }
@@ -993,15 +994,16 @@ inline int active_blocks(size_t numel, int nblocks, int world) {
 // the crossover falls as the group grows.  Measured on MI355X with every rank
 // in one group launch (graph-captured), as the first size at which the
 // two-shot was faster in two rounds: W = 3 98304, W = 4 16384, W = 5 10240,
-// W = 6 6144, W = 7 4096, W = 8 3072 (e.g. W = 5 at 10240 values 13.6-13.8
-// against 14.2 us, W = 8 at 3072 12.0-12.6 against 12.7-13.1 us).
+// W = 6 6144, W = 7 5120, W = 8 3072 (e.g. W = 5 at 10240 values 13.6-13.8
+// against 14.2 us, W = 7 at 4096 12.8-13.0 against 12.7 and at 5120 13.2-13.4
+// against 16.2-16.4, W = 8 at 3072 12.4-12.6 against 12.8 us).
 inline size_t two_shot_min_numel(int world) {
     switch (world) {
         case 3: return 98304;
         case 4: return 16384;
         case 5: return 10240;
         case 6: return 6144;
-        case 7: return 4096;
+        case 7: return 5120;
         default: return 3072;
     }
 }

@@ -439,7 +439,7 @@ def test_algorithm_choice():
         assert ch4.algorithm_for(16_384) == hr.HR_ALGO_TWO_SHOT
         assert ch4.algorithm_for(4096) == hr.HR_ALGO_LL
         assert ch4.algorithm_for(4097) == hr.HR_ALGO_ONE_SHOT
-        for W, ll_max, first in ((3, 8192, 98_304), (5, 2048, 10_240), (6, 2048, 6144), (7, 2048, 4096),
+        for W, ll_max, first in ((3, 8192, 98_304), (5, 4096, 10_240), (6, 2560, 6144), (7, 2048, 5120),
                                  (8, 1536, 3072)):
             chw = hr.Channel(world_size=W, timeout_us=TIMEOUT_US)
             try:

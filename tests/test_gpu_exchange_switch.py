@@ -28,8 +28,8 @@ TIMEOUT_US = 2_000_000
 
 # the automatic choice as hr.h states it: LL up to LL_MAX[W] values, the
 # two-shot from TWO_MIN[W] values (W >= 3), the one-shot between
-LL_MAX = {2: 20480, 3: 8192, 4: 4096, 5: 2048, 6: 2048, 7: 2048, 8: 1536}
-TWO_MIN = {3: 98304, 4: 16384, 5: 10240, 6: 6144, 7: 4096, 8: 3072}
+LL_MAX = {2: 20480, 3: 8192, 4: 4096, 5: 4096, 6: 2560, 7: 2048, 8: 1536}
+TWO_MIN = {3: 98304, 4: 16384, 5: 10240, 6: 6144, 7: 5120, 8: 3072}
 
 
 def expected_algorithm(W, n):
