@@ -798,3 +798,40 @@ def test_default_rate_is_measured_once_per_device():
             ch.destroy()
     say(f"default pacing rates: {rates}")
     assert len(set(rates)) == 1 and 20_000 <= rates[0] <= 80_000
+
+
+def test_ll_graph_across_the_call_field_wrap(streams):
+    """Low-latency words carry the call number's low 15 bits.  With every
+    counter set 300 calls below 2^15, three replays of a 1000-call graph per
+    rank run real low-latency traffic through the field's wrap (call 2^15
+    has the field of call 0) and through the clearing calls 2^15 + 2 and
+    2^15 + 3, with fresh inputs before every replay; every output is compared
+    with the oracle and the counters end 3000 calls on."""
+    calls, n, replays = 1000, 10_240, 3
+    start = (1 << 15) - 300
+    ch = hr.Channel(timeout_us=TIMEOUT_US, algorithm=hr.HR_ALGO_LL)
+    try:
+        assert ch.algorithm_for(n) == hr.HR_ALGO_LL
+        xin = [torch.zeros((calls, n), dtype=torch.float16, device="cuda:0") for _ in range(2)]
+        outs = [torch.empty_like(x) for x in xin]
+        loopback(ch, xin[0][0], xin[1][0], outs[0][0], outs[1][0], streams)   # warm-up
+        _counters(ch, start)
+        graphs = [_capture(ch, r, xin[r], outs[r], streams[r]) for r in range(2)]
+        rng = np.random.default_rng(7)
+        for rep in range(replays):
+            xb = [rng.standard_normal((calls, n), dtype=np.float32).astype(np.float16).view(np.uint16)
+                  for _ in range(2)]
+            for r in range(2):
+                xin[r].copy_(to_dev(xb[r].reshape(-1)).view(calls, n))
+            torch.cuda.synchronize()
+            say(f"LL graph across the field wrap: replay {rep}, calls {start + 1 + rep * calls}..")
+            _replay_both(graphs, streams)
+            assert ch.status() == hr.HR_OK
+            ref = oracle.add(xb[0].reshape(-1), xb[1].reshape(-1))
+            for r in range(2):
+                assert_same_bits(to_host(outs[r]).reshape(-1), ref, f"replay {rep} rank {r}")
+        assert set(_counters(ch)) == {start + replays * calls}
+        del graphs
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
