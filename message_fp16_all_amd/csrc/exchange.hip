@@ -23,6 +23,8 @@
 // body of the workgroup index, launched either once per rank (the rank's
 // own kernel, as on its own GPU) or once for every rank of a loopback group
 // (the *_group_k kernels: rank r's workgroups are blocks r * nblocks ..).
+// The per-rank kernels take the arguments of their first loads as leading
+// scalars, which the build has preloaded into SGPRs.
 //
 // Channel memory
 //   host (pinned, device-mapped, fine-grained/coherent):
@@ -32,7 +34,8 @@
 //     flags, reduced-shard flags  [W rank][nblocks], one 128-byte line each:
 //            the 64-bit call number of the last slice that workgroup
 //            published
-//     low-latency slots [2 parity][W rank][2 halves][units] 16-byte words
+//     low-latency slots [2 parity][W rank][3 planes][units] 64-bit words,
+//            each three values and a 16-bit call field
 //     error word, abort word (one line each)
 //   device (HBM): epoch[W rank][nblocks] -- per-workgroup 64-bit call
 //     counter (see next_call_number), device error word.
