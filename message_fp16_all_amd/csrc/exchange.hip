@@ -524,6 +524,7 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
 
     // first publish batch loaded ahead, as in the one-shot
     constexpr size_t kBatch = static_cast<size_t>(kExchThreads) * kExchUnroll;
+    const uint64_t tl0 = HR_NOW();
     T x[kExchUnroll];
     load_batch<T>(in, ulo + tid, uhi, active, x);
 
@@ -531,6 +532,7 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
     if (e == 0) return;
     if (ll_clear_due(e)) ll_clear(a, b, e, 0);
     if (!active) return;
+    const uint64_t tl1 = HR_NOW();
     const int parity = static_cast<int>(e & 1u);
     const int rank = a.rank;
     __amdgpu_buffer_rsrc_t slot[W];
@@ -541,6 +543,7 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
 
     // A. publish (paced as the one-shot's)
     pace(a, b, (hi - lo) * 16u * W);
+    const uint64_t tl2 = HR_NOW();
     for (size_t v0 = ulo + tid;;) {
         store_batch<T>(slot[rank], v0, uhi, x);
         v0 += kBatch;
@@ -554,6 +557,7 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
     if (tid == 0)
         __hip_atomic_store(a.flags + (static_cast<size_t>(rank) * a.nblocks + b) * kFlagStride, e,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint64_t tl3 = HR_NOW();
 
     if (shard == rank) {
         // B. fold this rank's shard
@@ -563,6 +567,7 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
         }
         __syncthreads();
         if (s_status != 0) return;
+        const uint64_t tl4 = HR_NOW();
         const bool one_unit = uhi - ulo <= static_cast<size_t>(kExchThreads);  // own unit still in x[0]
         for (size_t v = ulo + tid; v < uhi; v += kExchThreads) {
             T xs[W];
@@ -593,6 +598,9 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
         if (tid == 0)
             __hip_atomic_store(a.flags2 + (static_cast<size_t>(rank) * a.nblocks + b) * kFlagStride, e,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        // timeline: entry, counter, pace done, flag raised, peers seen, shard
+        // published with flag 2; role 1 (the shard's owner)
+        tl_record(a, b, e, tl0, tl1, tl2, tl3, tl4, HR_NOW(), 1);
     } else {
         // C. gather shard `shard` from its owner
         if (tid < 64) {
@@ -601,6 +609,7 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
         }
         __syncthreads();
         if (s_status != 0) return;
+        const uint64_t tl4 = HR_NOW();
         for (size_t v0 = ulo + tid; v0 < uhi; v0 += static_cast<size_t>(kExchThreads) * kExchUnroll) {
             T x[kExchUnroll];
 #pragma unroll
@@ -616,6 +625,9 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
         }
         if (last && tail0 + tid < a.numel)
             static_cast<uint16_t *>(a.out)[tail0 + tid] = HostIO<uint16_t>::load(red, tail0 + tid);
+        // timeline: entry, counter, pace done, flag raised, owner's flag 2
+        // seen, shard copied; role 2 (a gathering rank)
+        tl_record(a, b, e, tl0, tl1, tl2, tl3, tl4, HR_NOW(), 2);
     }
 }
 

@@ -8,6 +8,9 @@ rank's calls captured in its own graph, both graphs released together by a
 device-side gate -- and prints, per workload, the median and 90th percentile
 of every phase over the calls of one replay.
 
+Also, for groups of four and eight ranks in one launch, the two-shot: the
+phases of its last-ending workgroup and of the owner of the same shard part.
+
 Phases of a one-shot workgroup: entry (its start after the call's first
 workgroup), counter (loading the first input batch and advancing the call
 counter), pace (its turn on the host link), publish (slot stores, their
@@ -120,6 +123,99 @@ def run(lib, n, algorithm, calls, fresh_inputs):
     return rec, elapsed, algo
 
 
+def run_group(lib, world, n, algorithm, calls):
+    """Every rank of a `world`-rank channel in one launch per call
+    (hr_allreduce_group_f16), `calls` calls captured in one graph, released
+    by a device-side gate; returns the records, the replay's time and the
+    algorithm the calls took."""
+    import torch
+    ch = hr.Channel(world_size=world, timeout_us=2_000_000, algorithm=algorithm)
+    nb = ch.info().num_blocks
+    s = torch.cuda.Stream()
+    try:
+        xs = [torch.from_numpy(inputs.gaussian(n, 1.0, 6, r, 0).view(np.int16)).view(torch.float16).cuda()
+              for r in range(world)]
+        outs = [torch.empty_like(t) for t in xs]
+        buf = torch.zeros(calls * world * nb * WORDS, dtype=torch.int64, device="cuda:0")
+        hr._check(lib.hr_timeline_attach(buf.data_ptr(), calls), "hr_timeline_attach")
+        for _ in range(3):
+            ch.allreduce_group(xs, outs, s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(calls):
+                ch.allreduce_group(xs, outs, s)
+        gate_stream = torch.cuda.Stream()
+        elapsed = 0.0
+        for rep in range(3):
+            torch.cuda.synchronize()
+            buf.zero_()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(gate_stream):
+                torch.cuda._sleep(60_000_000)
+                gate = torch.cuda.Event()
+                gate.record(gate_stream)
+            s.wait_event(gate)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            with torch.cuda.stream(s):
+                g.replay()
+            e1.record(s)
+            torch.cuda.synchronize()
+            elapsed = e0.elapsed_time(e1) * 1e-3
+        if ch.status() != hr.HR_OK:
+            raise RuntimeError(hr.hr_status_str(ch.status()))
+        del g
+        rec = buf.cpu().numpy().view(np.uint64).reshape(calls, world, nb, WORDS)
+        algo = ch.algorithm_for(n)
+        lib.hr_timeline_attach(None, 0)
+    finally:
+        torch.cuda.synchronize()
+        ch.destroy()
+    return rec, elapsed, algo
+
+
+def analyse_two_shot(rec, elapsed):
+    """Phases of the two-shot's last-ending workgroup (usually a gathering
+    rank's) and of the owner of the same shard part in the same call."""
+    calls, world, nb, _ = rec.shape
+    active = rec[..., 7] != 0
+    t = rec[..., :6].astype(np.int64)
+    e = rec[..., 7]
+    order = np.argsort(np.where(active, e, np.iinfo(np.uint64).max).min(axis=(1, 2)))
+    t, active, role = t[order], active[order], rec[..., 6][order]
+    big = np.iinfo(np.int64).max
+    start = np.where(active, t[..., 0], big).min(axis=(1, 2))
+    end = np.where(active, t[..., 5], 0).max(axis=(1, 2))
+    ticks_per_us = (end[-1] - start[0]) / (elapsed * 1e6)
+    flat_end = np.where(active, t[..., 5], 0).reshape(calls, -1)
+    crit = flat_end.argmax(axis=1)
+    cr, cb = crit // nb, crit % nb                      # rank and workgroup of the critical one
+    tc = t[np.arange(calls), cr, cb]
+    # the owner of that workgroup's shard part: the rank whose role there is 1
+    own_rank = np.array([int(np.argmax(role[k, :, cb[k]] == 1)) for k in range(calls)])
+    to = t[np.arange(calls), own_rank, cb]
+    ph = {"entry": tc[:, 0] - start,
+          "counter": tc[:, 1] - tc[:, 0],
+          "pace (turn on the link)": tc[:, 2] - tc[:, 1],
+          "publish (stores, ack, flag)": tc[:, 3] - tc[:, 2],
+          "its wait (owner: peers' flags; other: the owner's flag 2)": tc[:, 4] - tc[:, 3],
+          "its last step (owner: reads, fold, shard and flag 2; other: shard copy)": tc[:, 5] - tc[:, 4],
+          "the shard owner: publish done to peers' flags seen": to[:, 4] - to[:, 3],
+          "the shard owner: reads, fold, shard and flag 2": to[:, 5] - to[:, 4],
+          "the owner's flag 2 raised to this workgroup seeing it": tc[:, 4] - to[:, 5],
+          "gap to the next call's first workgroup": np.concatenate([start[1:] - end[:-1], [0]]),
+          "call period (start to next start)": np.concatenate([np.diff(start), [0]])}
+    skip = calls // 10
+    rows = []
+    for name, v in ph.items():
+        v = v[skip:-1] / ticks_per_us
+        rows.append((name, float(np.median(v)), float(np.percentile(v, 90))))
+    crit_role = role[np.arange(calls), cr, cb][skip:]
+    nact = int(active[skip:].sum(axis=(1, 2)).max())
+    return rows, elapsed * 1e6 / calls, ticks_per_us, nact, float(np.mean(crit_role == 2))
+
+
 def analyse(rec, elapsed, algo):
     calls = rec.shape[0]
     active = rec[..., 7] != 0
@@ -170,6 +266,18 @@ def main(argv=None):
     cases = [("two ranks, N = 10240 (2 x 5120), fresh inputs per call, LL", 10_240, hr.HR_ALGO_AUTO, True),
              ("two ranks, N = 10240, one-shot", 10_240, hr.HR_ALGO_ONE_SHOT, True),
              ("two ranks, N = 131072 (32 x 4096), one-shot", 131_072, hr.HR_ALGO_AUTO, False)]
+    for world, n in ((4, 4096), (8, 4096)):
+        rec, elapsed, algo = run_group(lib, world, n, hr.HR_ALGO_TWO_SHOT, args.calls)
+        rows, per_call, tpu, nact, gather = analyse_two_shot(rec, elapsed)
+        print(f"\n### {world} ranks in one group launch, N = {n}, two-shot: graph of {args.calls} calls\n")
+        print(f"{per_call:.3f} us per call from HIP events; {nact} active workgroups per call "
+              f"(all ranks); clock {tpu:.2f} ticks/us; the last-ending workgroup was a gathering "
+              f"rank's in {100 * gather:.0f} % of the calls\n")
+        print("| phase | median us | p90 us |")
+        print("|---|---|---|")
+        for name, med, p90 in rows:
+            print(f"| {name} | {med:.3f} | {p90:.3f} |")
+        sys.stdout.flush()
     for title, n, algorithm, fresh in cases:
         rec, elapsed, algo = run(lib, n, algorithm, args.calls, fresh)
         rows, per_call, tpu, nact, polls = analyse(rec, elapsed, algo)
