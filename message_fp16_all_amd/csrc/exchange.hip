@@ -267,14 +267,22 @@ __device__ __forceinline__ uint64_t next_call_number(uint64_t prev) {
 // requests in order, so without pacing every flag and every read request
 // queues behind all of the call's slot writes; paced, the queue stays
 // short, each workgroup's handshake completes early and the reads of early
-// slices overlap the writes of later ones.  The first kPaceBurst + 1
-// workgroups start together: the link is idle when a call starts, and
-// writes reach its rate only with a few slices in flight.
+// slices overlap the writes of later ones.  The first burst + 1 workgroups
+// start together: the link is idle when a call starts, and writes reach its
+// rate only with a few slices in flight.  A one-shot call whose workgroups
+// each carry at most one unit per lane starts five together (kPaceBurstSmall),
+// others three (kPaceBurst).  Measured on MI355X, two ranks on loopback,
+// graph-captured, on two boxes, burst 2 / 4: 256 KiB 16.59-16.66 /
+// 16.49-16.50 us, 64 KiB 8.44-8.53 / 8.20-8.28 us; but 16 MiB per rank
+// 723 / 781-841 us, and the group two-shot at W = 4 and 8 ranks 1-1.5 us
+// slower with 4: their slices are larger, and a wider burst fills the
+// link's request queue.
 constexpr int kPaceBurst = 2;
+constexpr int kPaceBurstSmall = 4;
 
-__device__ __forceinline__ void pace(const ExchArgs &a, int b, uint64_t slice_bytes) {
-    if (a.pace_q16 == 0 || b <= kPaceBurst) return;
-    const uint64_t wait = (static_cast<uint64_t>(b - kPaceBurst) * slice_bytes * a.pace_q16) >> 16;
+__device__ __forceinline__ void pace(const ExchArgs &a, int b, uint64_t slice_bytes, int burst = kPaceBurst) {
+    if (a.pace_q16 == 0 || b <= burst) return;
+    const uint64_t wait = (static_cast<uint64_t>(b - burst) * slice_bytes * a.pace_q16) >> 16;
     const long long t0 = wall_clock64();
     while (static_cast<uint64_t>(wall_clock64() - t0) < wait) __builtin_amdgcn_s_sleep(1);
 }
@@ -421,7 +429,10 @@ __device__ __forceinline__ void exchange_body(const ExchArgs &a, const int b) {
 
     // 1. publish this rank's slice into its host slot (write-through),
     //    paced so that each workgroup's handshake and reads start early
-    pace(a, b, (hi - lo) * 16u * W);
+    // one unit per lane in every workgroup: the decode sizes (the split
+    // depends on numel alone, so every rank paces alike)
+    const bool small_slices = nvec <= static_cast<size_t>(a.nactive) * kExchThreads;
+    pace(a, b, (hi - lo) * 16u * W, small_slices ? kPaceBurstSmall : kPaceBurst);
     const uint64_t tl2 = HR_NOW();
     for (size_t v0 = ulo + tid;;) {
         store_batch<T>(slot[rank], v0, uhi, x);
