@@ -93,6 +93,7 @@ constexpr int kMaxWorld = 8;
 constexpr int kMinActivePolls = 16;                // W * minimum active workgroups
 constexpr uint32_t kAbortAfterUs = 20;             // waits read the abort word only after this long
 constexpr uint32_t kLLLeadNs = 400;                // an LL poll's lead over the words it should find
+constexpr uint32_t kLLFloorNs = 450;               // least hold of an LL poll in a per-rank launch
 constexpr size_t kLine = 128;                     // bytes per flag / word line
 constexpr size_t kFlagStride = kLine / sizeof(uint64_t);  // flags are 64-bit call numbers
 
@@ -113,7 +114,8 @@ struct ExchArgs {
     const uint32_t *abort_w;  // device view of the host abort word
     uint64_t timeout_ticks;
     uint64_t abort_after_ticks;  // waits shorter than this do not read the abort word
-    uint32_t ll_lead_ticks;   // LL: a read's lead over the last word it should find
+    uint16_t ll_lead_ticks;   // LL: a read's lead over the last word it should find
+    uint16_t ll_floor_ticks;  // LL: the least hold before the first poll (per-rank launches)
     uint32_t pace_q16;        // wall-clock ticks per byte of a paced publish, x 2^16 (0: unpaced)
     int rank;
     int world;
@@ -794,11 +796,24 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
     // one that reaches host memory before the peer's words costs a second
     // round trip.  The link carries all W ranks' words (24 bytes per unit)
     // at the channel's pacing rate; the poll leaves ll_lead_ticks early, the
-    // time its request takes to reach host memory
+    // time its request takes to reach host memory.
+    // Ranks launched separately start their calls up to about a microsecond
+    // apart, and a short hold lets them fall into a cycle: the rank that
+    // starts first polls too early, pays a second round trip, ends last and
+    // so starts the next call last, when its peer repeats the mistake.  The
+    // floor on the hold (ll_floor_ticks, zero for a group launch, whose ranks
+    // start together) gives the first poll room for that skew.  Measured on
+    // MI355X, two ranks at 4096 values, graph-captured: 4.48-4.55 us per
+    // call without the floor (5.97 once), 4.25-4.36 us with 450 ns, and
+    // 4.38-4.45 us with 300 or 600 ns.  Without the floor the skews of
+    // consecutive calls correlated at -0.55 to -0.85 and the last lane to
+    // finish polled twice in 76-97 % of the calls; with 450 ns its poll
+    // phase fell from 3.0 to 2.2 us (median).
     if (has && a.pace_q16 != 0) {
         const uint64_t drain = (static_cast<uint64_t>(W) * nunits * 24u * a.pace_q16) >> 16;
-        if (drain > a.ll_lead_ticks) {
-            const uint64_t hold = drain - a.ll_lead_ticks;
+        uint64_t hold = drain > a.ll_lead_ticks ? drain - a.ll_lead_ticks : 0u;
+        if (hold < a.ll_floor_ticks) hold = a.ll_floor_ticks;
+        if (hold != 0u) {
             const long long tw = wall_clock64();
             while (static_cast<uint64_t>(wall_clock64() - tw) < hold) __builtin_amdgcn_s_sleep(1);
         }
@@ -1142,7 +1157,8 @@ struct hr_channel_s {
     uint32_t timeout_us;
     uint64_t timeout_ticks;
     uint64_t abort_after_ticks;
-    uint32_t ll_lead_ticks;
+    uint16_t ll_lead_ticks;
+    uint16_t ll_floor_ticks;
     uint32_t link_mbps;        // pacing rate, or HR_LINK_UNPACED
     uint32_t pace_q16;         // wall-clock ticks per byte x 2^16, 0 when unpaced
     void *host_base;           // hipHostMalloc'ed region (host address)
@@ -1169,6 +1185,12 @@ struct DeviceGuard {
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ns nanoseconds in ticks of a clock of clock_khz, at most 65535.
+uint16_t ticks16(uint32_t ns, int clock_khz) {
+    const uint64_t t = static_cast<uint64_t>(ns) * static_cast<uint64_t>(clock_khz) / 1000000u;
+    return static_cast<uint16_t>(t < 65535u ? t : 65535u);
+}
 
 // The pacing rate (MB/s) for the host link: the rate at which it carries
 // writes while reads run the other way, which is what a paced exchange's
@@ -1293,7 +1315,8 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->timeout_us = timeout_us;
     ch->timeout_ticks = static_cast<uint64_t>(timeout_us) * static_cast<uint64_t>(clock_khz) / 1000u;
     ch->abort_after_ticks = static_cast<uint64_t>(kAbortAfterUs) * static_cast<uint64_t>(clock_khz) / 1000u;
-    ch->ll_lead_ticks = static_cast<uint32_t>(static_cast<uint64_t>(kLLLeadNs) * static_cast<uint64_t>(clock_khz) / 1000000u);
+    ch->ll_lead_ticks = ticks16(kLLLeadNs, clock_khz);
+    ch->ll_floor_ticks = ticks16(kLLFloorNs, clock_khz);
     ch->link_mbps = cfg->link_mbps;  // 0: the device's measured rate, below
 
     const size_t slot_bytes = 2 * static_cast<size_t>(world) * ch->stride * sizeof(uint16_t);
@@ -1365,7 +1388,7 @@ ExchArgs call_args(hr_channel ch, int rank, size_t numel, Algo *algo_out) {
     a.abort_w = reinterpret_cast<const uint32_t *>(ch->host_dev + ch->abort_off);
     a.timeout_ticks = ch->timeout_ticks;
     a.abort_after_ticks = ch->abort_after_ticks;
-    a.ll_lead_ticks = ch->ll_lead_ticks;
+    a.ll_lead_ticks = ch->ll_lead_ticks;  // the floor is set by per-rank calls only
     a.pace_q16 = ch->pace_q16;
     a.rank = rank;
     a.world = ch->world_size;
@@ -1399,6 +1422,7 @@ hr_status allreduce_impl(hr_channel ch, int rank, const void *in, void *out, siz
     ExchArgs a = call_args(ch, rank, numel, &algo);
     a.in = in;
     a.out = out;
+    a.ll_floor_ticks = ch->ll_floor_ticks;
     launch_exchange_w<E>(a, aligned(in, 16) && aligned(out, 16), algo, reinterpret_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? HR_OK : HR_ERR_HIP;
 }

@@ -10,6 +10,8 @@ of every phase over the calls of one replay.
 
 Also, for groups of four and eight ranks in one launch, the two-shot: the
 phases of its last-ending workgroup and of the owner of the same shard part.
+For the two-rank LL cases it also prints how far apart the ranks' calls start
+and, per rank, how often a lane 0 needed a second poll.
 
 Phases of a one-shot workgroup: entry (its start after the call's first
 workgroup), counter (loading the first input batch and advancing the call
@@ -256,6 +258,30 @@ def analyse(rec, elapsed, algo):
     return rows, per_call_us, ticks_per_us, nact, float(np.median(polls))
 
 
+def analyse_ll_ranks(rec, ticks_per_us):
+    """Two-rank LL calls, rank by rank: how far rank 1's first workgroup
+    starts after rank 0's, and, per rank, the share of calls in which some
+    active workgroup's lane 0 needed a second poll, with the median skew of
+    those calls.  Returns (skew median, p10, p90 in us, {rank: (share, median
+    skew of those calls)}); the replay's first tenth is skipped."""
+    calls = rec.shape[0]
+    active = rec[..., 7] != 0
+    t = rec[..., :6].astype(np.int64)
+    e = rec[..., 7]
+    order = np.argsort(np.where(active, e, np.iinfo(np.uint64).max).min(axis=(1, 2)))
+    t, active, polls = t[order], active[order], rec[..., 6][order].astype(np.int64)
+    big = np.iinfo(np.int64).max
+    start = np.where(active, t[..., 0], big).min(axis=2)               # [calls, rank]
+    skip = calls // 10
+    skew = (start[skip:, 1] - start[skip:, 0]) / ticks_per_us
+    out = {}
+    for r in range(rec.shape[1]):
+        extra = (np.where(active[skip:, r], polls[skip:, r], 0) >= 2).any(axis=1)
+        share = float(extra.mean())
+        out[r] = (share, float(np.median(skew[extra])) if extra.any() else float("nan"))
+    return (float(np.median(skew)), float(np.percentile(skew, 10)), float(np.percentile(skew, 90))), out
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--calls", type=int, default=1000)
@@ -264,6 +290,7 @@ def main(argv=None):
     ensure_built(args.rebuild)
     lib = load_timeline_library()
     cases = [("two ranks, N = 10240 (2 x 5120), fresh inputs per call, LL", 10_240, hr.HR_ALGO_AUTO, True),
+             ("two ranks, N = 4096 (one token), fresh inputs per call, LL", 4096, hr.HR_ALGO_AUTO, True),
              ("two ranks, N = 10240, one-shot", 10_240, hr.HR_ALGO_ONE_SHOT, True),
              ("two ranks, N = 131072 (32 x 4096), one-shot", 131_072, hr.HR_ALGO_AUTO, False)]
     for world, n in ((4, 4096), (8, 4096)):
@@ -289,6 +316,13 @@ def main(argv=None):
         print("|---|---|---|")
         for name, med, p90 in rows:
             print(f"| {name} | {med:.3f} | {p90:.3f} |")
+        if algo == hr.HR_ALGO_LL:
+            (sm, s10, s90), ranks = analyse_ll_ranks(rec, tpu)
+            print(f"\nRank 1's first workgroup starts {sm:+.3f} us after rank 0's (median; p10 "
+                  f"{s10:+.3f}, p90 {s90:+.3f}).")
+            for r, (share, sk) in ranks.items():
+                print(f"Rank {r}: some lane 0 polled twice or more in {100 * share:.0f} % of the calls "
+                      f"(median skew of those calls {sk:+.3f} us).")
         sys.stdout.flush()
 
 
