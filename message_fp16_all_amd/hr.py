@@ -296,6 +296,29 @@ def workspace(G: int, numel: int, dtype=None, device=0):
 
 
 # ----------------------------------------------------- torch marshalling
+#
+# An eager call's host time is HIP's kernel launch (about 3 us) plus this
+# marshalling, so the per-call helpers keep to attribute reads: torch and its
+# two element types are looked up once, dtypes are compared by identity
+# (torch dtypes are singletons), and a Channel binds its entry points once.
+# Measured on MI355X, host time per enqueued Channel.allreduce: 4.62-4.76 us
+# with an import and equality compares per call, 4.22-4.33 us as here, and
+# 3.28-3.76 us for the bare ctypes call.
+
+_torch = None
+_F16 = None
+_BF16 = None
+
+
+def _tm():
+    """The torch module, imported on first use (with its two dtypes)."""
+    global _torch, _F16, _BF16
+    if _torch is None:
+        import torch
+        _F16, _BF16 = torch.float16, torch.bfloat16
+        _torch = torch
+    return _torch
+
 
 def _check(st: int, where: str):
     if st != HR_OK:
@@ -303,9 +326,10 @@ def _check(st: int, where: str):
 
 
 def _f16_ptr(t, name: str, dtype=None) -> int:
-    import torch
-    want = torch.float16 if dtype is None else dtype
-    if t.dtype != want:
+    if _torch is None:
+        _tm()
+    want = _F16 if dtype is None else dtype
+    if t.dtype is not want:
         raise TypeError(f"{name}: expected {want}, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name}: expected a device tensor")
@@ -319,9 +343,9 @@ def _stream_handle(stream, tensor=None) -> int:
     device of ``tensor`` (or the current device).  torch's raw query returns
     the handle without building a Stream object, which costs more than the
     library call itself; the public call is the fallback."""
-    import torch
     if stream is not None:
-        return int(stream.cuda_stream)
+        return stream.cuda_stream
+    torch = _tm()
     dev = tensor.get_device() if tensor is not None else torch.cuda.current_device()
     raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
     if raw is not None:
@@ -332,10 +356,10 @@ def _stream_handle(stream, tensor=None) -> int:
 def reduce(tensors, out, stream=None):
     """out = left fold of ``tensors`` (all torch.float16, or all
     torch.bfloat16, same numel) on ``stream``."""
-    import torch
+    _tm()
     n = out.numel()
-    bf = out.dtype == torch.bfloat16
-    dt = torch.bfloat16 if bf else torch.float16
+    bf = out.dtype is _BF16
+    dt = _BF16 if bf else _F16
     ptrs = []
     for i, t in enumerate(tensors):
         if t.numel() != n:
@@ -379,6 +403,11 @@ class Channel:
         self.world_size = world_size
         self.handle = hr_create_channel(device, world_size, max_numel, num_blocks, timeout_us,
                                         algorithm, link_mbps)
+        lib = load()
+        _tm()
+        # the per-rank entry point of each element type, bound once
+        self._per_rank = {_F16: (lib.hr_allreduce_f16, "hr_allreduce_f16"),
+                          _BF16: (lib.hr_allreduce_bf16, "hr_allreduce_bf16")}
 
     def allreduce(self, rank: int, inp, out, stream=None):
         """One rank's call; torch.float16 or torch.bfloat16 tensors.
@@ -391,26 +420,27 @@ class Channel:
         the others spin: the call ends at the channel's watchdog with the
         sticky HR_ERR_TIMEOUT.  Enqueue nothing on the null stream between
         the ranks' calls, or use ``allreduce_group``."""
-        import torch
         n = inp.numel()
         if out.numel() != n:
             raise ValueError("in and out differ in numel")
-        bf = inp.dtype == torch.bfloat16
-        dt = torch.bfloat16 if bf else torch.float16
-        fn, name = (hr_allreduce_bf16, "hr_allreduce_bf16") if bf else (hr_allreduce_f16, "hr_allreduce_f16")
-        _check(fn(self.handle, rank, _f16_ptr(inp, "in", dt), _f16_ptr(out, "out", dt), n,
-                  _stream_handle(stream, out)), name)
+        dt = inp.dtype
+        fn, name = self._per_rank.get(dt, self._per_rank[_F16])
+        if dt is not _BF16:
+            dt = _F16                     # anything else is refused as not float16
+        st = fn(self.handle, rank, _f16_ptr(inp, "in", dt), _f16_ptr(out, "out", dt), n,
+                _stream_handle(stream, out))
+        if st != HR_OK:
+            raise HrError(st, name)
         return out
 
     def allreduce_group(self, ins, outs, stream=None):
         """Every rank's call in one launch (loopback): ``ins[r]``/``outs[r]``
         are rank r's torch.float16 or torch.bfloat16 tensors."""
-        import torch
         if len(ins) != self.world_size or len(outs) != self.world_size:
             raise ValueError(f"expected {self.world_size} inputs and outputs")
         n = ins[0].numel()
-        bf = ins[0].dtype == torch.bfloat16
-        dt = torch.bfloat16 if bf else torch.float16
+        bf = ins[0].dtype is _BF16
+        dt = _BF16 if bf else _F16
         for r in range(self.world_size):
             if ins[r].numel() != n or outs[r].numel() != n:
                 raise ValueError(f"rank {r}: every input and output must hold {n} values")
