@@ -144,15 +144,16 @@ typedef struct {
                              library keeps the rate for every later such
                              channel on that device, for the life of the
                              process (HR_DEFAULT_LINK_MBPS if the
-                             measurement fails).  The
-                             one-shot and the two-shot start workgroup b's
-                             publish b - 2 slices later than workgroups
-                             0..2's, a slice taking world_size x slice bytes
-                             / link_mbps, so that each workgroup's flag and
-                             reads are not queued behind every other
-                             workgroup's writes (the link carries requests in
-                             order) and the reads of early slices overlap
-                             the writes of later ones.
+                             measurement fails).  The one-shot and the
+                             two-shot start workgroup b's publish b - k
+                             slices later than workgroups 0..k's (k = 4 for
+                             one-shot calls that give every lane at most one
+                             16-byte unit, 2 otherwise), a slice taking
+                             world_size x slice bytes / link_mbps, so that
+                             each workgroup's flag and reads are not queued
+                             behind every other workgroup's writes (the link
+                             carries requests in order) and the reads of
+                             early slices overlap the writes of later ones.
                              A rate above the real one only lets the writes
                              queue again; one well below it delays the call.
                              HR_LINK_UNPACED: no pacing.  HR_LINK_CALIBRATE:
@@ -244,8 +245,9 @@ HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_channel *out
  * Enqueues exactly one kernel on `stream`.  Its workgroups each own one
  * contiguous slice of the numel values: they copy the slice of `in` into this
  * rank's host slot of the current parity (paced at the channel's link rate),
- * make the stores visible at system scope, raise their ready flag, wait (watchdog-bounded) for every peer's
- * flag of the same call, read the peers' slices from their host slots and
+ * make the stores visible at system scope, raise their ready flag, wait
+ * (watchdog-bounded) for every peer's flag of the same call, read the peers'
+ * slices from their host slots and
  * write the left fold x0 + x1 + ... in rank order, one binary16 rounding per
  * add, to `out` (for two ranks fl16(x0 + x1), the 1Cat-vLLM page's
  * "Purpose").  Parity comes from a device-resident per-workgroup call
