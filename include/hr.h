@@ -448,6 +448,32 @@ HR_API hr_status hr_channel_status(hr_channel ch);
  */
 HR_API hr_status hr_channel_abort(hr_channel ch);
 
+/*
+ * hr_channel_timeout_info -- after HR_ERR_TIMEOUT: which peers a rank's wait
+ * never heard from.
+ *
+ * The openinfer page ("Description") makes a wedged collective fail loudly
+ * and name the peers that never arrived.  When a wait for the peers'
+ * publishes (their ready flags, or their low-latency words) reaches the
+ * watchdog, the kernel records three things in one 64-bit word of the
+ * channel's host memory: the rank whose wait expired, the set of peers
+ * whose publish it had not seen, and the call number.  When several waits
+ * expire, the last record stays.  A two-shot rank waiting for a shard
+ * owner's folded shard records nothing: that wait expires only because some
+ * publish never arrived, and the owner's own wait records that.
+ *
+ * rank:      the rank whose wait expired, or -1 when nothing is recorded.
+ * peer_mask: bit q is set when rank q's publish never arrived; 0 when
+ *            nothing is recorded.
+ * call:      the call number's low 48 bits (a channel's first call on each
+ *            rank is number 1); 0 when nothing is recorded.
+ * Read it once the rank streams have finished (hr_channel_status then
+ * reports HR_ERR_TIMEOUT).  The allocation-free group call records nothing
+ * here; its status word is its whole report.  Host-only; never blocks.
+ * Errors: HR_ERR_INVALID_ARG for a null argument.
+ */
+HR_API hr_status hr_channel_timeout_info(hr_channel ch, int *rank, uint32_t *peer_mask, uint64_t *call);
+
 /* hr_channel_get_info -- fill *info with the channel's layout (read-only). */
 HR_API hr_status hr_channel_get_info(hr_channel ch, hr_channel_info *info);
 

@@ -112,6 +112,7 @@ struct ExchArgs {
     uint32_t *dev_error;      // HBM
     uint32_t *host_error;     // device view of the host error word
     const uint32_t *abort_w;  // device view of the host abort word
+    uint64_t *diag;           // device view of the host timeout record, or null
     uint64_t timeout_ticks;
     uint64_t abort_after_ticks;  // waits shorter than this do not read the abort word
     uint16_t ll_lead_ticks;   // LL: a read's lead over the last word it should find
@@ -214,13 +215,26 @@ __device__ __forceinline__ bool aborted(const ExchArgs &a, uint64_t waited) {
     return __shfl(ab, 0) != 0;
 }
 
+// After a wait timed out: the channel's timeout record takes the peers whose
+// signal the wait was still missing (bit q = rank q), this rank and the call
+// number's low 48 bits, packed into one 64-bit word written by one
+// system-scope store, so the host never reads a mix of two records.  Several
+// workgroups may time out on one call; the last record stays.
+__device__ __forceinline__ void record_missing(const ExchArgs &a, uint64_t e, unsigned missing) {
+    if (a.diag == nullptr) return;
+    const uint64_t w = (e << 16) | (static_cast<uint64_t>(a.rank & 0xFF) << 8) | (missing & 0xFFu);
+    __hip_atomic_store(a.diag, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Wait, in the first wave, until flag[q][b] >= e for every rank q whose bit
 // is set in `mask` (one lane per rank, wrap-safe compare), or the abort word
 // is set, or the watchdog expires.  Returns 0, HR_ERR_ABORTED or
 // HR_ERR_TIMEOUT, the same in every lane of the wave; lane 0 records an
-// error in both error words.
+// error in both error words and, when `record` is set (the waits for peers'
+// publishes, not the two-shot's wait for a shard owner, which only follows
+// from a missing publish), which peers' flags never arrived.
 __device__ __forceinline__ uint32_t wait_flags(const ExchArgs &a, const uint64_t *flag_base, int b, uint64_t e,
-                                               unsigned mask) {
+                                               unsigned mask, bool record = true) {
     const int lane = threadIdx.x;
     const bool polls = lane < kMaxWorld && ((mask >> lane) & 1u);
     const uint64_t *pf = flag_base + (static_cast<size_t>(polls ? lane : 0) * a.nblocks + b) * kFlagStride;
@@ -243,6 +257,10 @@ __device__ __forceinline__ uint32_t wait_flags(const ExchArgs &a, const uint64_t
             break;
         }
         __builtin_amdgcn_s_sleep(1);
+    }
+    if (status == HR_ERR_TIMEOUT && record) {
+        const unsigned missing = static_cast<unsigned>(__ballot(polls && !done));  // lane q polls rank q
+        if (lane == 0) record_missing(a, e, missing);
     }
     if (lane == 0 && status != 0) {
         __hip_atomic_store(a.dev_error, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -617,7 +635,7 @@ __device__ __forceinline__ void exchange2_body(const ExchArgs &a, const int b) {
     } else {
         // C. gather shard `shard` from its owner
         if (tid < 64) {
-            const uint32_t st = wait_flags(a, a.flags2, b, e, 1u << shard);
+            const uint32_t st = wait_flags(a, a.flags2, b, e, 1u << shard, false);
             if (tid == 0) s_status = st;
         }
         __syncthreads();
@@ -857,6 +875,14 @@ __device__ __forceinline__ void exchange_ll_body(const ExchArgs &a, const int b)
             break;
         }
         __builtin_amdgcn_s_sleep(kLLSleep);
+    }
+    if (__any(status == HR_ERR_TIMEOUT)) {
+        // the peers whose words some lane of this wave never saw
+        unsigned missing = 0;
+#pragma unroll
+        for (int q = 0; q < W; ++q)
+            if (__any((pending >> q) & 1u)) missing |= 1u << q;
+        if (tid % 64 == 0) record_missing(a, e64, missing);
     }
     if (status != 0 && tid % 64 == 0) {
         __hip_atomic_store(&s_status, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1164,7 +1190,7 @@ struct hr_channel_s {
     void *host_base;           // hipHostMalloc'ed region (host address)
     unsigned char *host_dev;   // the same region as seen by the device
     int algorithm;             // HR_ALGO_*
-    size_t flags_off, flags2_off, reduced_off, ll_off, ll_stride, error_off, abort_off, host_bytes;
+    size_t flags_off, flags2_off, reduced_off, ll_off, ll_stride, error_off, abort_off, diag_off, host_bytes;
     void *dev_base;            // hipMalloc: epochs[world][nblocks] (uint64), then the error word
     uint64_t *dev_epochs;
     uint32_t *dev_error;
@@ -1329,7 +1355,8 @@ extern "C" HR_API hr_status hr_create_channel(const hr_channel_config *cfg, hr_c
     ch->ll_stride = ll_stride_for(max_numel);
     ch->error_off = ch->ll_off + round_up(2 * static_cast<size_t>(world) * ch->ll_stride * sizeof(uint64_t), kLine);
     ch->abort_off = ch->error_off + kLine;
-    ch->host_bytes = ch->abort_off + kLine;
+    ch->diag_off = ch->abort_off + kLine;  // the timeout record (record_missing)
+    ch->host_bytes = ch->diag_off + kLine;
 
     // The call counters are zeroed on a private stream, so creating a channel
     // never waits for other work on the device (such as another channel's
@@ -1386,6 +1413,7 @@ ExchArgs call_args(hr_channel ch, int rank, size_t numel, Algo *algo_out) {
     a.dev_error = ch->dev_error;
     a.host_error = reinterpret_cast<uint32_t *>(ch->host_dev + ch->error_off);
     a.abort_w = reinterpret_cast<const uint32_t *>(ch->host_dev + ch->abort_off);
+    a.diag = reinterpret_cast<uint64_t *>(ch->host_dev + ch->diag_off);
     a.timeout_ticks = ch->timeout_ticks;
     a.abort_after_ticks = ch->abort_after_ticks;
     a.ll_lead_ticks = ch->ll_lead_ticks;  // the floor is set by per-rank calls only
@@ -1522,6 +1550,23 @@ extern "C" HR_API hr_status hr_channel_abort(hr_channel ch) {
     __atomic_store_n(reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(ch->host_base) + ch->abort_off), 1u,
                      __ATOMIC_RELEASE);
     __atomic_thread_fence(__ATOMIC_SEQ_CST);
+    return HR_OK;
+}
+
+extern "C" HR_API hr_status hr_channel_timeout_info(hr_channel ch, int *rank, uint32_t *peer_mask,
+                                                    uint64_t *call) {
+    if (ch == nullptr || rank == nullptr || peer_mask == nullptr || call == nullptr) return HR_ERR_INVALID_ARG;
+    const uint64_t w = __atomic_load_n(
+        reinterpret_cast<uint64_t *>(static_cast<unsigned char *>(ch->host_base) + ch->diag_off), __ATOMIC_ACQUIRE);
+    if (w == 0) {
+        *rank = -1;
+        *peer_mask = 0;
+        *call = 0;
+    } else {
+        *rank = static_cast<int>((w >> 8) & 0xFFu);
+        *peer_mask = static_cast<uint32_t>(w & 0xFFu);
+        *call = w >> 16;
+    }
     return HR_OK;
 }
 

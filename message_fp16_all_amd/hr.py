@@ -48,7 +48,7 @@ EXPORTS = ("hr_create_channel", "hr_allreduce_f16", "hr_reduce_f16", "hr_channel
            "hr_loopback_stream_create", "hr_loopback_stream_destroy",
            "hr_reduce_bf16", "hr_allreduce_bf16", "hr_admit", "hr_route_str", "hr_decode_numel",
            "hr_workspace_stride", "hr_exchange_algorithm", "hr_allreduce_group_f16",
-           "hr_allreduce_group_bf16", "hr_allreduce_group_noalloc_f16")
+           "hr_allreduce_group_bf16", "hr_allreduce_group_noalloc_f16", "hr_channel_timeout_info")
 
 HR_ROUTE_HOST = 0
 HR_DECLINE_DISABLED = 1
@@ -137,6 +137,8 @@ def load() -> ctypes.CDLL:
     lib.hr_channel_status.argtypes = [vp]
     lib.hr_exchange_algorithm.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
     lib.hr_channel_abort.argtypes = [vp]
+    lib.hr_channel_timeout_info.argtypes = [vp, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_uint32),
+                                            ctypes.POINTER(ctypes.c_uint64)]
     lib.hr_channel_get_info.argtypes = [vp, ctypes.POINTER(hr_channel_info)]
     lib.hr_destroy.argtypes = [vp]
     lib.hr_loopback_stream_create.argtypes = [ctypes.c_int, ctypes.POINTER(vp)]
@@ -239,6 +241,16 @@ def hr_exchange_algorithm(ch: int, numel: int) -> int:
 
 def hr_channel_abort(ch: int) -> int:
     return load().hr_channel_abort(ch)
+
+
+def hr_channel_timeout_info(ch: int):
+    """(rank, peer_mask, call) of the channel's timeout record; rank is -1
+    when nothing is recorded (raises HrError)."""
+    rank, mask, call = ctypes.c_int(-1), ctypes.c_uint32(0), ctypes.c_uint64(0)
+    st = load().hr_channel_timeout_info(ch, ctypes.byref(rank), ctypes.byref(mask), ctypes.byref(call))
+    if st != HR_OK:
+        raise HrError(st, "hr_channel_timeout_info")
+    return rank.value, mask.value, call.value
 
 
 def hr_channel_get_info(ch: int) -> hr_channel_info:
@@ -456,6 +468,15 @@ class Channel:
 
     def abort(self):
         _check(hr_channel_abort(self.handle), "hr_channel_abort")
+
+    def timeout_info(self):
+        """After HR_ERR_TIMEOUT: (rank whose wait expired, [ranks whose
+        publish never arrived], call number), or None if nothing is
+        recorded."""
+        rank, mask, call = hr_channel_timeout_info(self.handle)
+        if rank < 0:
+            return None
+        return rank, [q for q in range(self.world_size) if (mask >> q) & 1], call
 
     def info(self) -> hr_channel_info:
         return hr_channel_get_info(self.handle)

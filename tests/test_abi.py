@@ -108,6 +108,9 @@ def test_channel_validation_before_any_device_call():
     assert hr.hr_channel_status(None) == hr.HR_ERR_INVALID_ARG
     assert hr.hr_channel_abort(None) == hr.HR_ERR_INVALID_ARG
     assert lib.hr_channel_get_info(None, None) == hr.HR_ERR_INVALID_ARG
+    r, m, c = ctypes.c_int(), ctypes.c_uint32(), ctypes.c_uint64()
+    assert lib.hr_channel_timeout_info(None, ctypes.byref(r), ctypes.byref(m),
+                                       ctypes.byref(c)) == hr.HR_ERR_INVALID_ARG
     assert hr.hr_destroy(None) == hr.HR_OK
     assert lib.hr_loopback_stream_create(-1, ctypes.byref(h)) == hr.HR_ERR_INVALID_ARG
     assert lib.hr_loopback_stream_create(0, None) == hr.HR_ERR_INVALID_ARG

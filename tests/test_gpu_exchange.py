@@ -213,6 +213,8 @@ def test_peer_never_arrives_times_out(streams, algorithm):
         assert dt < 5.0
         # the timed-out kernel left out unwritten
         assert torch.all(out == 3.0)
+        # the timeout record: rank 0 waited, rank 1 never published, call 1
+        assert ch.timeout_info() == (0, [1], 1)
         # sticky: the next call is refused without a launch
         with pytest.raises(hr.HrError) as ei:
             ch.allreduce(1, x, out, streams[1])
@@ -646,6 +648,7 @@ def test_stale_peer_values_do_not_release(streams, algorithm, stale):
         streams[0].synchronize()
         assert ch.status() == hr.HR_ERR_TIMEOUT
         assert torch.all(out == 3.0), "a stale value released the waiter"
+        assert ch.timeout_info() == (0, [1], e & ((1 << 48) - 1))
     finally:
         torch.cuda.synchronize()
         ch.destroy()

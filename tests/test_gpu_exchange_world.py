@@ -155,6 +155,7 @@ def test_missing_rank_times_out_every_waiting_rank(algo):
         xs = [to_dev(b) for b in xb]
         outs = [torch.full_like(x, 3.0) for x in xs]
         torch.cuda.synchronize()
+        assert ch.timeout_info() is None
         for r in range(W - 1):                     # rank W-1 never arrives
             ch.allreduce(r, xs[r], outs[r], streams[r])
         for s in streams:
@@ -162,6 +163,9 @@ def test_missing_rank_times_out_every_waiting_rank(algo):
         assert ch.status() == hr.HR_ERR_TIMEOUT
         for r in range(W - 1):
             assert torch.all(outs[r] == 3.0)
+        # the timeout record names the missing rank and the call (the first)
+        rank, missing, call = ch.timeout_info()
+        assert rank in range(W - 1) and missing == [W - 1] and call == 1, (rank, missing, call)
         with pytest.raises(hr.HrError) as ei:
             ch.allreduce(W - 1, xs[W - 1], outs[W - 1], streams[W - 1])
         assert ei.value.status == hr.HR_ERR_TIMEOUT
