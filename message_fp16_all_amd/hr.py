@@ -442,8 +442,18 @@ class Channel:
         st = fn(self.handle, rank, _f16_ptr(inp, "in", dt), _f16_ptr(out, "out", dt), n,
                 _stream_handle(stream, out))
         if st != HR_OK:
-            raise HrError(st, name)
+            raise HrError(st, self._where(name, st))
         return out
+
+    def _where(self, name: str, st: int) -> str:
+        """The call's name, with the timeout record when the channel holds one."""
+        if st != HR_ERR_TIMEOUT:
+            return name
+        info = self.timeout_info()
+        if info is None:
+            return name
+        rank, missing, call = info
+        return f"{name} (rank {rank} waited at call {call} for ranks {missing})"
 
     def allreduce_group(self, ins, outs, stream=None):
         """Every rank's call in one launch (loopback): ``ins[r]``/``outs[r]``
@@ -460,7 +470,9 @@ class Channel:
         op = [_f16_ptr(t, f"outs[{r}]", dt) for r, t in enumerate(outs)]
         fn, name = ((hr_allreduce_group_bf16, "hr_allreduce_group_bf16") if bf
                     else (hr_allreduce_group_f16, "hr_allreduce_group_f16"))
-        _check(fn(self.handle, ip, op, n, _stream_handle(stream, outs[0])), name)
+        st = fn(self.handle, ip, op, n, _stream_handle(stream, outs[0]))
+        if st != HR_OK:
+            raise HrError(st, self._where(name, st))
         return outs
 
     def status(self) -> int:

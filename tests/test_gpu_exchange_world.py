@@ -169,6 +169,7 @@ def test_missing_rank_times_out_every_waiting_rank(algo):
         with pytest.raises(hr.HrError) as ei:
             ch.allreduce(W - 1, xs[W - 1], outs[W - 1], streams[W - 1])
         assert ei.value.status == hr.HR_ERR_TIMEOUT
+        assert f"for ranks [{W - 1}]" in str(ei.value)   # the error names the missing rank
     finally:
         torch.cuda.synchronize()
         ch.destroy()
