@@ -85,6 +85,17 @@ int main(int argc, char **argv)
         CHECK_HIP(hipStreamSynchronize((hipStream_t)s0));
         CHECK_HIP(hipStreamSynchronize((hipStream_t)s1));
         CHECK_HR(hr_channel_status(ch));
+        {   /* no wait timed out, so there is no timeout record */
+            int trank = 0;
+            uint32_t tmask = 1;
+            uint64_t tcall = 1;
+            CHECK_HR(hr_channel_timeout_info(ch, &trank, &tmask, &tcall));
+            if (trank != -1 || tmask != 0 || tcall != 0) {
+                fprintf(stderr, "unexpected timeout record: rank %d mask %u call %llu\n", trank,
+                        (unsigned)tmask, (unsigned long long)tcall);
+                return 4;
+            }
+        }
         CHECK_HIP(hipMemcpy(res + n, out[1], n * 2, hipMemcpyDeviceToHost));
         CHECK_HIP(hipMemcpy(res + 2 * n, out[2], n * 2, hipMemcpyDeviceToHost));
         CHECK_HR(hr_destroy(ch));
