@@ -36,7 +36,8 @@
 //            published
 //     low-latency slots [2 parity][W rank][3 planes][units] 64-bit words,
 //            each three values and a 16-bit call field
-//     error word, abort word (one line each)
+//     error word, abort word, timeout record (one line each; the record
+//            names the peers a timed-out wait never heard from)
 //   device (HBM): epoch[W rank][nblocks] -- per-workgroup 64-bit call
 //     counter (see next_call_number), device error word.
 //
